@@ -1,0 +1,9 @@
+"""CPU oracle of the Qwen3 attention block -- test infrastructure only.
+
+Importable only from tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg.  The product path never imports it.
+"""
+from .qwen3_attn_oracle import (  # noqa: F401
+    decode, gqa_attention, linear, merge_heads, prefill, project_norm_rope,
+    rms_norm, rope, rope_inv_freq, softmax, split_heads,
+)
