@@ -1,0 +1,149 @@
+/*
+ * qwen3_attn.h -- C ABI of the MI355X (gfx950) Qwen3 self-attention block.
+ *
+ * The block (cited by page title and section):
+ *   - q/k/v projections without bias, weights stored [out, in]
+ *     ("Hand-Writing a Vision-Language Model, Part 1", section "Attention:
+ *     Grouped-Query Attention"; "Learning 10", section "Part 2 - tensor by
+ *     tensor");
+ *   - per-head RMSNorm of q and of k over d_head with learned gains
+ *     q_norm / k_norm, eps inside the square root ("Qwen 3 From Scratch",
+ *     section "The idea"; "Qwen3 Architecture Layer-by-Layer", section
+ *     "Primitives - Qwen3RMSNorm");
+ *   - RoPE on q and k, pairing dimension i with i + d_head/2, angle
+ *     p * rope_theta^(-2i/d_head) ("Assembling a large model from scratch",
+ *     section "The complete code": rope_cos_sin / rotate_half);
+ *   - causal grouped-query attention, query head h reading KV head
+ *     h / (n_q / n_kv), scores scaled by 1/sqrt(d_head), softmax in fp32
+ *     (same sections; mask tril(diagonal = S - T));
+ *   - heads merged in head order and projected by o_proj [d, n_q*d_head].
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *     of the descriptor's dtype (fp32 or bf16) unless stated otherwise;
+ *     positions are int32.  Accumulation is always fp32.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call is
+ *     asynchronous on that stream and never synchronises the host.
+ *   - Arguments are validated on the host before anything is enqueued: on any
+ *     non-OK status nothing has been launched.  Device-side preconditions
+ *     (positions in range) are documented, not checked.  Kernel faults
+ *     surface at the caller's next synchronisation of the stream.
+ *   - The forward calls allocate nothing; scratch memory is the caller's
+ *     workspace.  Two calls in flight at once need two workspaces.
+ */
+#ifndef QWEN3_ATTN_H
+#define QWEN3_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct qwen3_attn qwen3_attn_t; /* opaque handle */
+
+typedef enum {
+  QWEN3_ATTN_F32 = 0,  /* fp32 storage, fp32 arithmetic */
+  QWEN3_ATTN_BF16 = 1  /* bf16 storage, fp32 accumulation */
+} qwen3_attn_dtype;
+
+typedef enum {
+  QWEN3_ATTN_OK = 0,
+  QWEN3_ATTN_EINVAL = 1,       /* null pointer, non-positive size, bad combination */
+  QWEN3_ATTN_EUNSUPPORTED = 2, /* valid, but outside what the kernels implement */
+  QWEN3_ATTN_ENOMEM = 3,       /* device allocation in create failed */
+  QWEN3_ATTN_EWORKSPACE = 4,   /* workspace missing or smaller than required */
+  QWEN3_ATTN_EHIP = 5          /* a HIP runtime call or kernel launch failed */
+} qwen3_attn_status;
+
+/* Block configuration.  Supported: d_head == 128; n_q % n_kv == 0;
+ * d_model % 128 == 0; n_q / n_kv <= 16 for decode; eps >= 0; rope_theta > 1. */
+typedef struct {
+  int32_t d_model;   /* hidden size d */
+  int32_t n_q;       /* query heads */
+  int32_t n_kv;      /* key/value heads */
+  int32_t d_head;    /* head dim (128) */
+  float eps;         /* RMSNorm epsilon of q_norm / k_norm (1e-6 for Qwen3) */
+  double rope_theta; /* RoPE base (1e6 for Qwen3) */
+  int32_t dtype;     /* a qwen3_attn_dtype */
+} qwen3_attn_desc;
+
+/* Device pointers, row-major [out, in] as stored in the checkpoints:
+ *   wq [n_q*d_head, d_model], wk / wv [n_kv*d_head, d_model],
+ *   wo [d_model, n_q*d_head], q_norm / k_norm [d_head]. */
+typedef struct {
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const void* q_norm;
+  const void* k_norm;
+} qwen3_attn_weights;
+
+/* Create a handle.  Validates `desc` on the host first (EINVAL /
+ * EUNSUPPORTED before any HIP call), then allocates handle-owned device
+ * memory and copies the weights into it on `stream` (q/k/v merged into one
+ * [(n_q+2*n_kv)*d_head, d_model] matrix).  The caller may free its weight
+ * buffers once `stream` has completed.  The handle is immutable afterwards.
+ * On error *out is set to NULL. */
+qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc,
+                                    const qwen3_attn_weights* weights,
+                                    void* stream, qwen3_attn_t** out);
+
+/* Bytes of workspace a forward call needs (0 if the arguments are invalid).
+ * Pure host computation, no HIP call.
+ *   is_decode = 0: prefill of B_or_N sequences of T tokens (cache_cap unused);
+ *   is_decode = 1: decode of B_or_N sequences (T must be 1), caches of
+ *                  cache_cap slots. */
+size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
+                                 int32_t B_or_N, int32_t T, int64_t cache_cap);
+
+/* Prefill: B sequences of T new tokens each, over EMPTY caches.
+ *   hidden    [B, T, d_model]
+ *   positions [B, T] int32, drives RoPE only (the mask is by token index:
+ *             token t sees cache slots 0..t)
+ *   k_cache, v_cache [B, n_kv, cache_cap, d_head]: token t's post-norm,
+ *             post-RoPE key and its value are written to slot t; slots
+ *             >= T are not touched.  Requires T <= cache_cap.
+ *   out       [B, T, d_model]
+ * Workspace layout after the call (informative, for tests): the rotated
+ * queries [B*T, n_q*d_head] then the merged attention output
+ * [B*T, n_q*d_head], both of the dtype. */
+qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,
+                                             const int32_t* positions,
+                                             void* k_cache, void* v_cache,
+                                             int64_t cache_cap, void* out,
+                                             int32_t B, int32_t T,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
+/* Decode: one new token for each of N sequences.
+ *   hidden    [N, d_model]
+ *   positions [N] int32 device array, positions[s] = L_s = the number of
+ *             tokens already cached for sequence s (0 allowed).  Precondition
+ *             (not checked, device data): 0 <= L_s < cache_cap.
+ *   k_cache, v_cache [N, n_kv, cache_cap, d_head]: slots 0..L_s-1 hold the
+ *             sequence's cached keys/values; the new token's key/value are
+ *             written to slot L_s and it attends to slots 0..L_s.
+ *   out       [N, d_model]
+ * Re-running the same call is idempotent (same slot, same values). */
+qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,
+                                            const int32_t* positions,
+                                            void* k_cache, void* v_cache,
+                                            int64_t cache_cap, void* out, int32_t N,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/* Free the handle's device memory (synchronises the device first so no
+ * enqueued work still reads it).  NULL is a no-op. */
+void qwen3_attn_destroy(qwen3_attn_t* h);
+
+/* Static description of a status code. */
+const char* qwen3_attn_status_string(qwen3_attn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QWEN3_ATTN_H */

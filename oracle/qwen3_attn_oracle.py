@@ -204,3 +204,34 @@ def decode(x, wq, wk, wv, wo, gq, gk, positions, k_cache, v_cache, *, n_q, n_kv,
         A[s] = merge_heads(gqa_attention(q[s], ks, vs))[0]
     Y = linear(A, wo, dtype)
     return dict(Y=Y, k_new=k[:, 0], v_new=v[:, 0], A=A, Q=q[:, 0])
+
+
+def prefill_rows(x, wq, wk, wv, wo, gq, gk, positions, rows, *, n_q, n_kv, dh=128,
+                 eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+    """The prefill output at selected tokens only, for full-size checks.
+
+    rows: list of (b, t).  Same definition as ``prefill``: keys/values of
+    tokens 0..t of sequence b, the query of token t, causal GQA over them,
+    then o_proj.  Returns Y [len(rows), d], A [len(rows), n_q*dh], and the
+    post-norm post-RoPE keys/values of every token up to the largest
+    sampled t of each sampled sequence: Kc[b], Vc[b] as [n_kv, t_max+1, dh].
+    """
+    seqs = sorted({b for b, _ in rows})
+    kv = {}
+    for b in seqs:
+        tmax = max(t for bb, t in rows if bb == b)
+        # keys/values of the needed prefix; the query projection is not needed here
+        _, k, v = project_norm_rope(x[b, :tmax + 1], wq[:0], wk, wv, gq, gk,
+                                    positions[b, :tmax + 1], n_q=0, n_kv=n_kv, dh=dh,
+                                    eps=eps, theta=theta, dtype=dtype)
+        kv[b] = (k, v)
+    A = np.empty((len(rows), n_q * dh), dtype)
+    for i, (b, t) in enumerate(rows):
+        q, _, _ = project_norm_rope(x[b, t:t + 1], wq, wk[:0], wv[:0], gq, gk,
+                                    positions[b, t:t + 1], n_q=n_q, n_kv=0, dh=dh,
+                                    eps=eps, theta=theta, dtype=dtype)
+        k, v = kv[b]
+        A[i] = merge_heads(gqa_attention(q, k[:t + 1], v[:t + 1]))[0]
+    Y = linear(A, wo, dtype)
+    return dict(Y=Y, A=A, Kc={b: np.transpose(kv[b][0], (1, 0, 2)) for b in seqs},
+                Vc={b: np.transpose(kv[b][1], (1, 0, 2)) for b in seqs})

@@ -1,0 +1,281 @@
+// Host side of the C ABI declared in include/qwen3_attn.h: argument
+// validation, workspace sizing, the handle's weight copy, and the launch
+// sequence of each forward call on the caller's stream.
+#include "qwen3_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <new>
+
+#include "kernels.hpp"
+
+struct qwen3_attn {
+  qwen3_attn_desc desc;
+  int device;
+  void* mem;         // one device allocation holding everything below
+  void* w_qkv;       // [(n_q + 2 n_kv) * 128, d]  (q rows, then k rows, then v rows)
+  void* w_o;         // [d, n_q * 128]
+  void* g_q;         // [128]
+  void* g_k;         // [128]
+  float* inv_freq;   // [64] theta^(-2i/128), rounded once from double
+  float inv_freq_host[64];
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(int32_t dtype) { return dtype == QWEN3_ATTN_F32 ? 4 : 2; }
+
+qwen3_attn_status check_desc(const qwen3_attn_desc* d) {
+  if (!d) return QWEN3_ATTN_EINVAL;
+  if (d->dtype != QWEN3_ATTN_F32 && d->dtype != QWEN3_ATTN_BF16) return QWEN3_ATTN_EINVAL;
+  if (d->d_model <= 0 || d->n_q <= 0 || d->n_kv <= 0 || d->d_head <= 0) return QWEN3_ATTN_EINVAL;
+  if (d->d_head % 2 != 0) return QWEN3_ATTN_EINVAL;
+  if (d->n_q % d->n_kv != 0) return QWEN3_ATTN_EINVAL;
+  if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return QWEN3_ATTN_EINVAL;
+  if (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta)) return QWEN3_ATTN_EINVAL;
+  if (d->d_head != 128) return QWEN3_ATTN_EUNSUPPORTED;
+  if (d->d_model % 128 != 0) return QWEN3_ATTN_EUNSUPPORTED;
+  if ((int64_t)(d->n_q + 2 * d->n_kv) * 128 > INT_MAX / 2) return QWEN3_ATTN_EUNSUPPORTED;
+  return QWEN3_ATTN_OK;
+}
+
+struct WsLayout {
+  size_t q_off, a_off, acc_off, ml_off, total;
+  int nchunk;
+};
+
+bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, int64_t cap,
+               WsLayout* L) {
+  if (check_desc(d) != QWEN3_ATTN_OK) return false;
+  if (n <= 0 || T <= 0) return false;
+  const size_t es = elem_size(d->dtype);
+  const size_t hq = (size_t)d->n_q * 128;
+  if (!is_decode) {
+    if ((int64_t)n * T > INT_MAX / 2) return false;
+    const size_t qb = align_up((size_t)n * T * hq * es);
+    L->q_off = 0;
+    L->a_off = qb;
+    L->acc_off = L->ml_off = 0;
+    L->nchunk = 0;
+    L->total = 2 * qb;
+    return true;
+  }
+  if (T != 1 || cap <= 0 || cap > INT_MAX) return false;
+  const int chunk = q3::decode_chunk_keys();
+  const int64_t nchunk = (cap + chunk - 1) / chunk;
+  const size_t n_rep = d->n_q / d->n_kv;
+  const size_t slots = (size_t)n * d->n_kv * nchunk * n_rep;
+  const size_t qb = align_up((size_t)n * hq * es);
+  L->q_off = 0;
+  L->a_off = qb;
+  L->acc_off = 2 * qb;
+  L->ml_off = L->acc_off + align_up(slots * 128 * sizeof(float));
+  L->total = L->ml_off + align_up(slots * 2 * sizeof(float));
+  L->nchunk = (int)nchunk;
+  return true;
+}
+
+qwen3_attn_status hip_status(hipError_t e) {
+  return e == hipSuccess ? QWEN3_ATTN_OK : QWEN3_ATTN_EHIP;
+}
+
+template <typename T>
+qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
+                              void* k_cache, void* v_cache, int64_t cap, void* out, int B,
+                              int T_len, char* ws, const WsLayout& L, hipStream_t s) {
+  const qwen3_attn_desc& d = h->desc;
+  const int M = B * T_len;
+  const int nqkv = (d.n_q + 2 * d.n_kv) * 128;
+  const int hq = d.n_q * 128;
+  T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
+  T* abuf = reinterpret_cast<T*>(ws + L.a_off);
+  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
+                    d.n_q, d.n_kv, cap, T_len, 0, d.eps};
+  hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
+                                        reinterpret_cast<const T*>(h->w_qkv), M, nqkv, d.d_model,
+                                        e, s);
+  if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
+                                  reinterpret_cast<const T*>(v_cache), abuf, B, T_len, d.n_q, d.n_kv,
+                                  cap, s);
+  if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
+                              M, d.d_model, hq, s);
+  return hip_status(r);
+}
+
+template <typename T>
+qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
+                             void* k_cache, void* v_cache, int64_t cap, void* out, int N, char* ws,
+                             const WsLayout& L, hipStream_t s) {
+  const qwen3_attn_desc& d = h->desc;
+  const int nqkv = (d.n_q + 2 * d.n_kv) * 128;
+  const int hq = d.n_q * 128;
+  T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
+  T* abuf = reinterpret_cast<T*>(ws + L.a_off);
+  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
+                    d.n_q, d.n_kv, cap, 1, 1, d.eps};
+  hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
+                                        reinterpret_cast<const T*>(h->w_qkv), N, nqkv, d.d_model,
+                                        e, s);
+  if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  q3::DecodeScratch sc{reinterpret_cast<float*>(ws + L.acc_off),
+                       reinterpret_cast<float*>(ws + L.ml_off), L.nchunk,
+                       q3::decode_chunk_keys()};
+  r = q3::launch_decode_attn<T>(qbuf, reinterpret_cast<const T*>(k_cache),
+                                reinterpret_cast<const T*>(v_cache), positions, abuf, N, d.n_q,
+                                d.n_kv, cap, sc, s);
+  if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
+                              N, d.d_model, hq, s);
+  return hip_status(r);
+}
+
+qwen3_attn_status check_handle_device(const qwen3_attn_t* h) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QWEN3_ATTN_EHIP;
+  return dev == h->device ? QWEN3_ATTN_OK : QWEN3_ATTN_EINVAL;
+}
+
+}  // namespace
+
+extern "C" {
+
+qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc, const qwen3_attn_weights* w,
+                                    void* stream, qwen3_attn_t** out) {
+  if (!out) return QWEN3_ATTN_EINVAL;
+  *out = nullptr;
+  qwen3_attn_status st = check_desc(desc);
+  if (st != QWEN3_ATTN_OK) return st;
+  if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->q_norm || !w->k_norm)
+    return QWEN3_ATTN_EINVAL;
+
+  qwen3_attn_t* h = new (std::nothrow) qwen3_attn_t();
+  if (!h) return QWEN3_ATTN_ENOMEM;
+  h->desc = *desc;
+  const size_t es = elem_size(desc->dtype);
+  const size_t d = desc->d_model, hq = (size_t)desc->n_q * 128, hkv = (size_t)desc->n_kv * 128;
+  const size_t b_wqkv = align_up((hq + 2 * hkv) * d * es);
+  const size_t b_wo = align_up(d * hq * es);
+  const size_t b_g = align_up(128 * es);
+  const size_t b_f = align_up(64 * sizeof(float));
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return QWEN3_ATTN_EHIP;
+  }
+  if (hipMalloc(&h->mem, b_wqkv + b_wo + 2 * b_g + b_f) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return QWEN3_ATTN_ENOMEM;
+  }
+  char* p = static_cast<char*>(h->mem);
+  h->w_qkv = p;
+  h->w_o = p + b_wqkv;
+  h->g_q = p + b_wqkv + b_wo;
+  h->g_k = p + b_wqkv + b_wo + b_g;
+  h->inv_freq = reinterpret_cast<float*>(p + b_wqkv + b_wo + 2 * b_g);
+  for (int i = 0; i < 64; ++i)
+    h->inv_freq_host[i] = static_cast<float>(std::pow(desc->rope_theta, -2.0 * i / 128.0));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wqkv = static_cast<char*>(h->w_qkv);
+  hipError_t r = hipMemcpyAsync(wqkv, w->wq, hq * d * es, hipMemcpyDeviceToDevice, s);
+  if (r == hipSuccess)
+    r = hipMemcpyAsync(wqkv + hq * d * es, w->wk, hkv * d * es, hipMemcpyDeviceToDevice, s);
+  if (r == hipSuccess)
+    r = hipMemcpyAsync(wqkv + (hq + hkv) * d * es, w->wv, hkv * d * es, hipMemcpyDeviceToDevice, s);
+  if (r == hipSuccess) r = hipMemcpyAsync(h->w_o, w->wo, d * hq * es, hipMemcpyDeviceToDevice, s);
+  if (r == hipSuccess) r = hipMemcpyAsync(h->g_q, w->q_norm, 128 * es, hipMemcpyDeviceToDevice, s);
+  if (r == hipSuccess) r = hipMemcpyAsync(h->g_k, w->k_norm, 128 * es, hipMemcpyDeviceToDevice, s);
+  if (r == hipSuccess)
+    r = hipMemcpyAsync(h->inv_freq, h->inv_freq_host, 64 * sizeof(float), hipMemcpyHostToDevice, s);
+  if (r == hipSuccess) r = hipStreamSynchronize(s);  // host staging of inv_freq must complete
+  if (r != hipSuccess) {
+    (void)hipFree(h->mem);
+    delete h;
+    return QWEN3_ATTN_EHIP;
+  }
+  *out = h;
+  return QWEN3_ATTN_OK;
+}
+
+size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode, int32_t B_or_N,
+                                 int32_t T, int64_t cache_cap) {
+  WsLayout L;
+  if (!ws_layout(desc, is_decode ? 1 : 0, B_or_N, T, cache_cap, &L)) return 0;
+  return L.total;
+}
+
+qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,
+                                             const int32_t* positions, void* k_cache,
+                                             void* v_cache, int64_t cache_cap, void* out,
+                                             int32_t B, int32_t T, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  if (!h || !hidden || !positions || !k_cache || !v_cache || !out) return QWEN3_ATTN_EINVAL;
+  if (B <= 0 || T <= 0 || cache_cap <= 0 || T > cache_cap) return QWEN3_ATTN_EINVAL;
+  if (B > 65535) return QWEN3_ATTN_EUNSUPPORTED;
+  WsLayout L;
+  if (!ws_layout(&h->desc, 0, B, T, cache_cap, &L)) return QWEN3_ATTN_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < L.total) return QWEN3_ATTN_EWORKSPACE;
+  qwen3_attn_status st = check_handle_device(h);
+  if (st != QWEN3_ATTN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (h->desc.dtype == QWEN3_ATTN_F32)
+    return run_prefill<float>(h, hidden, positions, k_cache, v_cache, cache_cap, out, B, T, ws, L,
+                              s);
+  return run_prefill<q3::bf16_t>(h, hidden, positions, k_cache, v_cache, cache_cap, out, B, T, ws,
+                                 L, s);
+}
+
+qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,
+                                            const int32_t* positions, void* k_cache,
+                                            void* v_cache, int64_t cache_cap, void* out,
+                                            int32_t N, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  if (!h || !hidden || !positions || !k_cache || !v_cache || !out) return QWEN3_ATTN_EINVAL;
+  if (N <= 0 || cache_cap <= 0) return QWEN3_ATTN_EINVAL;
+  if (N > 65535 || cache_cap > INT_MAX) return QWEN3_ATTN_EUNSUPPORTED;
+  if (!q3::decode_nrep_supported(h->desc.n_q / h->desc.n_kv)) return QWEN3_ATTN_EUNSUPPORTED;
+  WsLayout L;
+  if (!ws_layout(&h->desc, 1, N, 1, cache_cap, &L)) return QWEN3_ATTN_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < L.total) return QWEN3_ATTN_EWORKSPACE;
+  qwen3_attn_status st = check_handle_device(h);
+  if (st != QWEN3_ATTN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (h->desc.dtype == QWEN3_ATTN_F32)
+    return run_decode<float>(h, hidden, positions, k_cache, v_cache, cache_cap, out, N, ws, L, s);
+  return run_decode<q3::bf16_t>(h, hidden, positions, k_cache, v_cache, cache_cap, out, N, ws, L,
+                                s);
+}
+
+void qwen3_attn_destroy(qwen3_attn_t* h) {
+  if (!h) return;
+  int prev = -1;
+  const bool switched = hipGetDevice(&prev) == hipSuccess && prev != h->device &&
+                        hipSetDevice(h->device) == hipSuccess;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(h->mem);
+  if (switched) (void)hipSetDevice(prev);
+  delete h;
+}
+
+const char* qwen3_attn_status_string(qwen3_attn_status s) {
+  switch (s) {
+    case QWEN3_ATTN_OK: return "ok";
+    case QWEN3_ATTN_EINVAL: return "invalid argument";
+    case QWEN3_ATTN_EUNSUPPORTED: return "unsupported configuration";
+    case QWEN3_ATTN_ENOMEM: return "device allocation failed";
+    case QWEN3_ATTN_EWORKSPACE: return "workspace missing or too small";
+    case QWEN3_ATTN_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

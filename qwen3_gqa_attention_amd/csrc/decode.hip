@@ -1,0 +1,256 @@
+// Decode attention: one new query token per sequence over its KV cache.
+//
+// What it computes ("Assembling a large model from scratch", section "The
+// complete code": with a cache of L tokens the new token sits at position L
+// and sees keys 0..L; query head h reads KV head h / n_rep) -- split over key
+// chunks and merged with log-sum-exp weights, which reaches the same softmax
+// up to rounding order.
+//
+// The step is bound by HBM: every cached key/value row is read once, and the
+// n_rep query heads of a KV head share that read.  Grid = (key chunk, KV head,
+// sequence); chunks past a sequence's length exit at once.  Inside a
+// workgroup each wave streams a contiguous quarter of the chunk; within a
+// wave four 16-lane groups take interleaved keys and each lane owns 8 of the
+// 128 dims, so every key row is two coalesced 256-byte reads (K and V, bf16).
+// Scores are a dot product over the lane's 8 dims reduced across the 16
+// lanes; softmax statistics and the weighted V sum stay in fp32 registers.
+// The four groups, then the four waves, are merged in registers / LDS and one
+// partial (max, sum, weighted values) per chunk is written.  A second kernel
+// merges the chunks of each (sequence, query head).
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace q3 {
+
+constexpr int kDecodeChunk = 512;  // keys per workgroup
+constexpr int kDecodeUnroll = 2;   // keys per 16-lane group per iteration
+
+int decode_chunk_keys() { return kDecodeChunk; }
+
+template <typename T> struct RowSlice;  // 8 elements of a row
+template <> struct RowSlice<bf16_t> {
+  u32x4_v v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = ld16(p); }
+  __device__ __forceinline__ void zero() { v = u32x4_v{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ float at(int e) const {
+    const uint32_t w = v[e >> 1];
+    return (e & 1) ? hi_bf16(w) : lo_bf16(w);
+  }
+};
+template <> struct RowSlice<float> {
+  u32x4_v v0, v1;
+  __device__ __forceinline__ void load(const float* p) { v0 = ld16(p); v1 = ld16(p + 4); }
+  __device__ __forceinline__ void zero() { v0 = v1 = u32x4_v{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ float at(int e) const {
+    return __uint_as_float(e < 4 ? v0[e] : v1[e - 4]);
+  }
+};
+
+template <typename T, int NREP>
+__global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ Q,
+                                                          const T* __restrict__ Kc,
+                                                          const T* __restrict__ Vc,
+                                                          const int32_t* __restrict__ positions,
+                                                          float* __restrict__ part_acc,
+                                                          float* __restrict__ part_ml, int n_q,
+                                                          int n_kv, int64_t cap, int nchunk,
+                                                          float scale_log2) {
+  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int nkeys = positions[s] + 1;
+  const int k0 = c * kDecodeChunk;
+  if (k0 >= nkeys) return;
+  const int k1 = min(k0 + kDecodeChunk, nkeys);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, oct = lane & 15;
+  constexpr int SUB = kDecodeChunk / 4;
+  const int wk0 = k0 + wave * SUB;
+  const int wk1 = min(wk0 + SUB, k1);
+
+  float q[NREP][8];
+  {
+    const T* qp = Q + (size_t)s * n_q * kHeadDim + (size_t)g * NREP * kHeadDim + oct * 8;
+#pragma unroll
+    for (int r = 0; r < NREP; ++r) {
+      RowSlice<T> x;
+      x.load(qp + r * kHeadDim);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[r][e] = x.at(e) * scale_log2;
+    }
+  }
+  float m[NREP], l[NREP], acc[NREP][8];
+#pragma unroll
+  for (int r = 0; r < NREP; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+  }
+
+  const T* Kg = Kc + (size_t)(s * n_kv + g) * cap * kHeadDim + oct * 8;
+  const T* Vg = Vc + (size_t)(s * n_kv + g) * cap * kHeadDim + oct * 8;
+  constexpr int U = kDecodeUnroll;
+  for (int kb = wk0; kb < wk1; kb += 4 * U) {
+    RowSlice<T> kr[U], vr[U];
+    bool val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = kb + grp + 4 * u;
+      val[u] = key < wk1;
+      if (val[u]) {
+        kr[u].load(Kg + (size_t)key * kHeadDim);
+        vr[u].load(Vg + (size_t)key * kHeadDim);
+      } else {
+        kr[u].zero();
+        vr[u].zero();
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NREP; ++r) {
+      float sc[U];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(q[r][e], kr[u].at(e), d);
+        d = wave_xor_sum(d, 1, 8);
+        sc[u] = val[u] ? d : -INFINITY;
+        mx = fmaxf(mx, sc[u]);
+      }
+      if (mx == -INFINITY) continue;  // uniform within the 16-lane group
+      const float m_new = fmaxf(m[r], mx);
+      const float alpha = exp2f(m[r] - m_new);
+      m[r] = m_new;
+      l[r] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = exp2f(sc[u] - m_new);
+        l[r] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, vr[u].at(e), acc[r][e]);
+      }
+    }
+  }
+
+  // Merge the four 16-lane groups of the wave (lanes oct, oct+16, +32, +48).
+#pragma unroll
+  for (int r = 0; r < NREP; ++r) {
+    const float M = wave_xor_max(m[r], 16, 32);
+    const float sc = (m[r] == -INFINITY) ? 0.f : exp2f(m[r] - M);
+    l[r] = wave_xor_sum(l[r] * sc, 16, 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = wave_xor_sum(acc[r][e] * sc, 16, 32);
+    m[r] = M;
+  }
+
+  // Merge the four waves through LDS.
+  __shared__ float sm_ml[4][NREP][2];
+  __shared__ float sm_acc[4][NREP][kHeadDim];
+  if (grp == 0) {
+#pragma unroll
+    for (int r = 0; r < NREP; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[wave][r][oct * 8 + e] = acc[r][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < NREP; ++r) {
+      sm_ml[wave][r][0] = m[r];
+      sm_ml[wave][r][1] = l[r];
+    }
+  }
+  __syncthreads();
+  const size_t slot = ((size_t)(s * n_kv + g) * nchunk + c) * NREP;
+  for (int idx = tid; idx < NREP * kHeadDim; idx += 256) {
+    const int r = idx / kHeadDim, d = idx % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_ml[w][r][0]);
+    float a = 0.f, lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm_ml[w][r][0];
+      const float sc = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      a += sc * sm_acc[w][r][d];
+      lt += sc * sm_ml[w][r][1];
+    }
+    part_acc[(slot + r) * kHeadDim + d] = a;
+    if (d == 0) {
+      part_ml[(slot + r) * 2 + 0] = M;
+      part_ml[(slot + r) * 2 + 1] = lt;
+    }
+  }
+}
+
+// Merge the key chunks of each (sequence, query head): grid (n_q, N), 128 threads.
+template <typename T>
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part_acc,
+                                                             const float* __restrict__ part_ml,
+                                                             const int32_t* __restrict__ positions,
+                                                             T* __restrict__ Out, int n_q, int n_kv,
+                                                             int nchunk) {
+  const int head = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  const int n_rep = n_q / n_kv;
+  const int g = head / n_rep, r = head % n_rep;
+  const int nc = (positions[s] + 1 + kDecodeChunk - 1) / kDecodeChunk;
+  const size_t base = (size_t)(s * n_kv + g) * nchunk;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, part_ml[((base + c) * n_rep + r) * 2]);
+  float a = 0.f, lt = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const size_t sl = (base + c) * n_rep + r;
+    const float w = exp2f(part_ml[sl * 2] - M);
+    lt += w * part_ml[sl * 2 + 1];
+    a += w * part_acc[sl * kHeadDim + d];
+  }
+  Out[(size_t)s * n_q * kHeadDim + head * kHeadDim + d] = from_f32<T>(a / lt);
+}
+
+template <typename T, int NREP>
+static void launch_decode_nrep(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
+                               int N, int n_q, int n_kv, int64_t cap, const DecodeScratch& ws,
+                               hipStream_t s) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHeadDim));
+  hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(ws.nchunk, n_kv, N), dim3(256), 0, s, Q,
+                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, cap, ws.nchunk,
+                     scale_log2);
+}
+
+template <typename T>
+hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
+                              T* Out, int N, int n_q, int n_kv, int64_t cap,
+                              const DecodeScratch& ws, hipStream_t s) {
+  switch (n_q / n_kv) {
+    case 1: launch_decode_nrep<T, 1>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    case 2: launch_decode_nrep<T, 2>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    case 3: launch_decode_nrep<T, 3>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    case 4: launch_decode_nrep<T, 4>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    case 5: launch_decode_nrep<T, 5>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    case 6: launch_decode_nrep<T, 6>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    case 8: launch_decode_nrep<T, 8>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    case 16: launch_decode_nrep<T, 16>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(n_q, N), dim3(kHeadDim), 0, s, ws.part_acc,
+                     ws.part_ml, positions, Out, n_q, n_kv, ws.nchunk);
+  return hipGetLastError();
+}
+
+bool decode_nrep_supported(int n_rep) {
+  return n_rep == 1 || n_rep == 2 || n_rep == 3 || n_rep == 4 || n_rep == 5 || n_rep == 6 ||
+         n_rep == 8 || n_rep == 16;
+}
+
+template hipError_t launch_decode_attn<float>(const float*, const float*, const float*,
+                                              const int32_t*, float*, int, int, int, int64_t,
+                                              const DecodeScratch&, hipStream_t);
+template hipError_t launch_decode_attn<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
+                                               const int32_t*, bf16_t*, int, int, int, int64_t,
+                                               const DecodeScratch&, hipStream_t);
+
+}  // namespace q3

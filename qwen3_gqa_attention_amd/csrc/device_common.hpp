@@ -1,0 +1,105 @@
+// Device-side building blocks shared by the gfx950 kernels of the block:
+// storage types, MFMA wrappers with their lane layouts, conversions and
+// wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3 {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x16_v __attribute__((ext_vector_type(16)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 128;
+
+// ---------------------------------------------------------------------------
+// Conversions.  bf16 -> f32 is exact (a shift); f32 -> bf16 rounds to nearest
+// even (gfx950 v_cvt_pk_bf16_f32).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(bf16_t, b);
+}
+// Two f32 -> packed bf16x2 (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// ---------------------------------------------------------------------------
+// 32x32 MFMA, fp32 accumulate.  D[32x32] += A[32xK] * B[Kx32].
+//   A fragment: lane l holds row (l % 32), k-slice (l / 32) * KL .. + KL-1
+//   B fragment: lane l holds col (l % 32), the same k-slice
+//   D:          lane l, element i holds row 8*(i/4) + 4*(l/32) + (i%4),
+//               col (l % 32)
+// bf16: K = 16 per instruction, KL = 8 values per lane (one 16-byte load).
+// f32:  K = 2 per instruction,  KL = 1 value per lane.
+// Any permutation of k applied identically to A and B is harmless.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma32;
+
+template <> struct Mfma32<bf16_t> {
+  static constexpr int K = 16;
+  static constexpr int KL = 8;
+  typedef bf16x8_v frag;
+  __device__ __forceinline__ static f32x16_v run(const frag& a, const frag& b, f32x16_v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const bf16_t* p) {  // 16-byte aligned
+    return *reinterpret_cast<const frag*>(p);
+  }
+  __device__ __forceinline__ static frag zero() { return frag{}; }
+};
+
+template <> struct Mfma32<float> {
+  static constexpr int K = 2;
+  static constexpr int KL = 1;
+  typedef float frag;
+  __device__ __forceinline__ static f32x16_v run(frag a, frag b, f32x16_v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const float* p) { return *p; }
+  __device__ __forceinline__ static frag zero() { return 0.f; }
+};
+
+// Row of element i of a 32x32 MFMA accumulator held by lane l.
+__device__ __forceinline__ int mfma32_row(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte vector type used for global <-> LDS staging.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4_v ld16(const void* p) { return *reinterpret_cast<const u32x4_v*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4_v v) { *reinterpret_cast<u32x4_v*>(p) = v; }
+
+// xor-butterfly reductions across lanes.
+__device__ __forceinline__ float wave_xor_sum(float v, int mask_lo, int mask_hi) {
+  for (int m = mask_lo; m <= mask_hi; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_xor_max(float v, int mask_lo, int mask_hi) {
+  for (int m = mask_lo; m <= mask_hi; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+}  // namespace q3

@@ -1,0 +1,57 @@
+// Host-side launchers of the gfx950 kernels (implemented in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3 {
+
+typedef uint16_t bf16_t;
+
+// Epilogue of the fused q/k/v projection: per-head RMSNorm of q and k with
+// their gains, RoPE on q and k, then q to `q_out` and k/v into the caches.
+struct QkvEpilogue {
+  void* q_out;               // [rows, n_q*128]
+  void* k_cache;             // [seqs, n_kv, cap, 128]
+  void* v_cache;             // [seqs, n_kv, cap, 128]
+  const int32_t* positions;  // [rows] RoPE position of each row
+  const void* gq;            // [128] q_norm gain (dtype of the block)
+  const void* gk;            // [128] k_norm gain
+  const float* inv_freq;     // [64] theta^(-2i/128)
+  int n_q, n_kv;
+  int64_t cap;
+  int rows_per_seq;          // prefill: T (slot = row % T); decode: 1
+  int decode;                // 1: cache slot = positions[row]
+  float eps;
+};
+
+// q/k/v projection X[M,K] * Wqkv[N,K]^T with the fused epilogue; N = (n_q + 2 n_kv) * 128.
+template <typename T>
+hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K,
+                           const QkvEpilogue& e, hipStream_t s);
+
+// Plain projection C[M,N] = A[M,K] * W[N,K]^T (o_proj).
+template <typename T>
+hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, hipStream_t s);
+
+// Causal GQA flash attention over the freshly written caches.
+template <typename T>
+hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
+                                int n_q, int n_kv, int64_t cap, hipStream_t s);
+
+// Split-K decode attention: partial (max, sum, weighted values) per key chunk,
+// then the log-sum-exp merge into Out [N, n_q*128].
+struct DecodeScratch {
+  float* part_acc;  // [N, n_kv, nchunk, n_rep, 128]
+  float* part_ml;   // [N, n_kv, nchunk, n_rep, 2]
+  int nchunk;
+  int chunk;
+};
+int decode_chunk_keys();
+bool decode_nrep_supported(int n_rep);
+template <typename T>
+hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
+                              T* Out, int N, int n_q, int n_kv, int64_t cap,
+                              const DecodeScratch& ws, hipStream_t s);
+
+}  // namespace q3

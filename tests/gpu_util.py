@@ -1,0 +1,61 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP block
+through the C ABI binding, compare against the oracle with the pass bar."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import qwen3_gqa_attention_amd as q3
+from workloads import EPS, ROPE_THETA
+
+# Pass bar: fp32 max abs error <= 1e-4; bf16 max abs <= 2e-2 and rel L2 <= 1e-2.
+TOL = {"f32": dict(max_abs=1e-4, rel_l2=None), "bf16": dict(max_abs=2e-2, rel_l2=1e-2)}
+
+
+def torch_dtype(name):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def dev(a, dtype):
+    """Host float32 values (already representable in dtype) -> device tensor."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    return t.to(torch_dtype(dtype)) if dtype != "f32" else t
+
+
+def host(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def block_from_inputs(inp, n_q, n_kv, dtype) -> q3.Qwen3Attention:
+    return q3.Qwen3Attention(dev(inp["Wq"], dtype), dev(inp["Wk"], dtype), dev(inp["Wv"], dtype),
+                             dev(inp["Wo"], dtype), dev(inp["gq"], dtype), dev(inp["gk"], dtype),
+                             n_q=n_q, n_kv=n_kv, eps=EPS, rope_theta=ROPE_THETA)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    diff = got - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    nrm = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff) / nrm) if nrm > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def assert_close(got, ref, dtype, what):
+    max_abs, rel = errors(got, ref)
+    tol = TOL[dtype]
+    print(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    assert max_abs <= tol["max_abs"], f"{what}: max abs {max_abs:.3e} > {tol['max_abs']}"
+    if tol["rel_l2"] is not None:
+        assert rel <= tol["rel_l2"], f"{what}: rel L2 {rel:.3e} > {tol['rel_l2']}"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()

@@ -1,0 +1,101 @@
+"""C-ABI checks that need no GPU: exported symbols, host-side validation,
+workspace sizing and status strings.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import qwen3_gqa_attention_amd as q3
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qwen3_attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwen3_attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == sorted(q3.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(built_lib):
+    lib = ctypes.CDLL(built_lib)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def desc(**kw):
+    base = dict(d_model=1024, n_q=16, n_kv=8, d_head=128, eps=1e-6, rope_theta=1e6, dtype=q3.QWEN3_ATTN_BF16)
+    base.update(kw)
+    return q3.Qwen3AttnDesc(**base)
+
+
+WEIGHTS = q3.Qwen3AttnWeights(*([0x1000] * 6))   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q=12, n_kv=8), 1),          # n_q % n_kv != 0
+    (dict(n_q=0), 1),
+    (dict(n_kv=-1), 1),
+    (dict(d_model=0), 1),
+    (dict(d_head=127), 1),              # odd head dim
+    (dict(d_head=64), 2),               # valid but not implemented
+    (dict(d_model=1000), 2),            # d_model % 128 != 0
+    (dict(dtype=7), 1),
+    (dict(eps=-1.0), 1),
+    (dict(eps=float("nan")), 1),
+    (dict(rope_theta=0.5), 1),
+    (dict(rope_theta=float("inf")), 1),
+])
+def test_create_rejects_bad_descriptors_before_any_hip_call(built_lib, kw, status):
+    st, h = q3.qwen3_attn_create(desc(**kw), WEIGHTS, 0)
+    assert st == status and h == 0
+
+
+def test_create_rejects_null_weights(built_lib):
+    for i in range(6):
+        ptrs = [0x1000] * 6
+        ptrs[i] = 0
+        st, h = q3.qwen3_attn_create(desc(), q3.Qwen3AttnWeights(*ptrs), 0)
+        assert st == 1 and h == 0
+    lib = q3.lib()
+    assert lib.qwen3_attn_create(ctypes.byref(desc()), None, None, None) == 1
+
+
+def align(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_size_prefill_and_decode(built_lib):
+    d = desc()
+    assert q3.qwen3_attn_workspace_size(d, 0, 2, 2048, 0) == 2 * align(2 * 2048 * 2048 * 2)
+    d32 = desc(dtype=q3.QWEN3_ATTN_F32)
+    assert q3.qwen3_attn_workspace_size(d32, 0, 1, 128, 0) == 2 * align(128 * 2048 * 4)
+    # decode: q and merged output, then per-chunk partials (512-key chunks)
+    cap, N = 32832, 64
+    nchunk = -(-cap // 512)
+    slots = N * 8 * nchunk * 2
+    want = 2 * align(N * 2048 * 2) + align(slots * 128 * 4) + align(slots * 2 * 4)
+    assert q3.qwen3_attn_workspace_size(d, 1, N, 1, cap) == want
+
+
+@pytest.mark.parametrize("args", [(0, 0, 128, 0), (0, 2, 0, 0), (1, 4, 2, 100), (1, 4, 1, 0),
+                                  (1, 0, 1, 100)])
+def test_workspace_size_zero_for_invalid(built_lib, args):
+    assert q3.qwen3_attn_workspace_size(desc(), *args) == 0
+    assert q3.qwen3_attn_workspace_size(desc(n_q=12), 0, 1, 8, 0) == 0
+
+
+def test_forward_with_null_handle_is_einval(built_lib):
+    assert q3.qwen3_attn_forward_prefill(None, 1, 1, 1, 1, 16, 1, 1, 8, 1, 1 << 20, None) == 1
+    assert q3.qwen3_attn_forward_decode(None, 1, 1, 1, 1, 16, 1, 1, 1, 1 << 20, None) == 1
+    q3.qwen3_attn_destroy(None)   # NULL is a no-op
+
+
+def test_status_strings(built_lib):
+    for code in range(6):
+        assert q3.qwen3_attn_status_string(code)
+    assert q3.qwen3_attn_status_string(99) == "unknown status"

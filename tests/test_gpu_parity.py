@@ -1,0 +1,282 @@
+"""Parity of the HIP block (through the C ABI) with the fp64 CPU oracle.
+
+Reduced sizes span several 128-row / 64-key tiles and a ragged tail; the full
+workload sizes run in the same launch configuration as the benchmark and are
+checked on sampled rows (prefill) or sampled sequences (decode) that the
+oracle computes one by one.  Pass bar: fp32 max abs <= 1e-4; bf16 max abs <=
+2e-2 and relative L2 <= 1e-2.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, block_from_inputs, dev, host, say
+from workloads import (EPS, ROPE_THETA, WORKLOADS, decode_cache_host, decode_inputs,
+                       prefill_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(built_lib):
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def run_prefill_gpu(w, inp, B, T, *, cap_extra=64):
+    import torch
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    cap = T + cap_extra
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    kc = torch.full((B, w.n_kv, cap, 128), float("nan"), dtype=x.dtype, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    ws = torch.empty(blk.workspace_size(False, B, T), dtype=torch.uint8, device="cuda")
+    y = blk.prefill(x, pos, kc, vc, workspace=ws)
+    torch.cuda.synchronize()
+    es = 4 if w.dtype == "f32" else 2
+    qt = ws[: B * T * w.n_q * 128 * es].view(x.dtype).view(B, T, w.n_q, 128)
+    out = dict(Y=host(y), Kc=host(kc), Vc=host(vc), Q=host(qt))
+    blk.close()
+    return out
+
+
+def oracle_prefill(inp, w):
+    return oracle.prefill(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], inp["gq"],
+                          inp["gk"], inp["positions"], n_q=w.n_q, n_kv=w.n_kv, eps=EPS,
+                          theta=ROPE_THETA)
+
+
+PREFILL_CASES = [
+    (1, 1, 128),   # the tiny fp32 workload at its full size
+    (1, 2, 200),   # fp32, ragged over the 128-row and 32-key tiles
+    (2, 2, 300),   # 0.6B shape, ragged over 128-row / 64-key tiles
+    (3, 1, 520),   # 4B shape (n_rep 4)
+    (4, 1, 260),   # wide GQA (n_rep 16)
+    (2, 3, 1),     # one token per sequence
+    (2, 1, 33),
+    (2, 1, 64),
+]
+
+
+@pytest.mark.parametrize("idx,B,T", PREFILL_CASES)
+def test_prefill_parity(idx, B, T):
+    w = WORKLOADS[idx]
+    say(f"prefill parity: workload {idx} ({w.name}) B={B} T={T}")
+    inp = prefill_inputs(w, B=B, T=T)
+    got = run_prefill_gpu(w, inp, B, T)
+    ref = oracle_prefill(inp, w)
+    assert_close(got["Q"], ref["Q"], w.dtype, "q~ (post-norm, post-RoPE)")
+    assert_close(got["Kc"][:, :, :T], ref["Kc"], w.dtype, "k cache")
+    assert_close(got["Vc"][:, :, :T], ref["Vc"], w.dtype, "v cache")
+    assert np.all(np.isnan(got["Kc"][:, :, T:])), "cache slots >= T were written"
+    assert np.all(np.isnan(got["Vc"][:, :, T:])), "cache slots >= T were written"
+    assert_close(got["Y"], ref["Y"], w.dtype, "block output Y")
+
+
+def test_prefill_full_size_0p6b():
+    # The benchmark's workload, compared in full.
+    w = WORKLOADS[2]
+    say(f"prefill parity full size: {w.name}")
+    inp = prefill_inputs(w)
+    got = run_prefill_gpu(w, inp, w.B, w.T)
+    ref = oracle_prefill(inp, w)
+    assert_close(got["Kc"][:, :, :w.T], ref["Kc"], w.dtype, "k cache")
+    assert_close(got["Vc"][:, :, :w.T], ref["Vc"], w.dtype, "v cache")
+    assert_close(got["Y"], ref["Y"], w.dtype, "block output Y")
+
+
+@pytest.mark.parametrize("idx", [3, 4])
+def test_prefill_full_size_sampled_rows(idx):
+    w = WORKLOADS[idx]
+    say(f"prefill parity full size, sampled rows: {w.name}")
+    inp = prefill_inputs(w)
+    got = run_prefill_gpu(w, inp, w.B, w.T)
+    rng = np.random.default_rng(idx)
+    ts = sorted({0, 1, 31, 63, 64, 127, 128, 129, w.T // 2, w.T - 2, w.T - 1,
+                 *rng.integers(0, w.T, 6).tolist()})
+    rows = [(0, t) for t in ts]
+    ref = oracle.prefill_rows(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], inp["gq"],
+                              inp["gk"], inp["positions"], rows, n_q=w.n_q, n_kv=w.n_kv,
+                              eps=EPS, theta=ROPE_THETA)
+    assert_close(got["Kc"][0], ref["Kc"][0], w.dtype, "k cache (all tokens)")
+    assert_close(got["Vc"][0], ref["Vc"][0], w.dtype, "v cache (all tokens)")
+    assert_close(np.stack([got["Y"][0, t] for t in ts]), ref["Y"], w.dtype, "Y at sampled rows")
+
+
+def test_prefill_mha_case():
+    # n_kv == n_q: standard multi-head attention (n_rep = 1).
+    w = dataclasses.replace(WORKLOADS[2], n_q=8, n_kv=8)
+    inp = prefill_inputs(w, B=1, T=150)
+    got = run_prefill_gpu(w, inp, 1, 150)
+    ref = oracle_prefill(inp, w)
+    assert_close(got["Y"], ref["Y"], w.dtype, "Y (MHA)")
+
+
+def test_prefill_nonzero_positions():
+    # Positions drive RoPE only; an offset start still uses the causal-by-index mask.
+    w = WORKLOADS[2]
+    inp = prefill_inputs(w, B=2, T=70)
+    inp["positions"] = inp["positions"] + np.array([[5000], [31000]], np.int32)
+    got = run_prefill_gpu(w, inp, 2, 70)
+    ref = oracle_prefill(inp, w)
+    assert_close(got["Kc"][:, :, :70], ref["Kc"], w.dtype, "k cache")
+    assert_close(got["Y"], ref["Y"], w.dtype, "Y")
+
+
+def test_prefill_deterministic_and_causal():
+    w = WORKLOADS[2]
+    inp = prefill_inputs(w, B=1, T=200)
+    a = run_prefill_gpu(w, inp, 1, 200)
+    b = run_prefill_gpu(w, inp, 1, 200)
+    np.testing.assert_array_equal(a["Y"], b["Y"])
+    # Perturbing tokens after t leaves outputs 0..t bitwise unchanged.
+    t = 77
+    pert = dict(inp)
+    x = inp["X"].copy()
+    x[:, t + 1:] = prefill_inputs(w, B=1, T=200, seed=99)["X"][:, t + 1:]
+    pert["X"] = x
+    c = run_prefill_gpu(w, pert, 1, 200)
+    np.testing.assert_array_equal(c["Y"][:, : t + 1], a["Y"][:, : t + 1])
+    assert not np.array_equal(c["Y"][:, t + 1:], a["Y"][:, t + 1:])
+
+
+# ------------------------------------------------------------------------- decode
+def run_decode_gpu(w, inp, kc_host, vc_host, cap):
+    import torch
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    kc = dev(kc_host, w.dtype)
+    vc = dev(vc_host, w.dtype)
+    y = blk.decode(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    out = dict(Y=host(y), kc=kc, vc=vc)
+    blk.close()
+    return out
+
+
+def check_decode(w, inp, kc_host, vc_host, got):
+    ref = oracle.decode(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], inp["gq"], inp["gk"],
+                        inp["positions"], kc_host, vc_host, n_q=w.n_q, n_kv=w.n_kv, eps=EPS,
+                        theta=ROPE_THETA)
+    assert_close(got["Y"], ref["Y"], w.dtype, "decode Y")
+    L = inp["positions"]
+    kc = host(got["kc"])
+    vc = host(got["vc"])
+    k_new = np.stack([kc[s, :, L[s]] for s in range(len(L))])
+    v_new = np.stack([vc[s, :, L[s]] for s in range(len(L))])
+    assert_close(k_new, ref["k_new"], w.dtype, "new k in cache slot L")
+    assert_close(v_new, ref["v_new"], w.dtype, "new v in cache slot L")
+    # the cached prefix is untouched
+    for s in range(len(L)):
+        np.testing.assert_array_equal(kc[s, :, : L[s]], kc_host[s, :, : L[s]])
+
+
+@pytest.mark.parametrize("dtype,n_q,n_kv", [("bf16", 16, 8), ("f32", 16, 8), ("bf16", 32, 8),
+                                            ("bf16", 64, 4), ("bf16", 40, 8), ("bf16", 8, 8)])
+def test_decode_parity_ragged(dtype, n_q, n_kv):
+    w = dataclasses.replace(WORKLOADS[5], dtype=dtype, n_q=n_q, n_kv=n_kv)
+    say(f"decode parity: dtype={dtype} n_q={n_q} n_kv={n_kv}")
+    lens = np.array([0, 1, 127, 511, 512, 513, 1030, 2047], np.int32)
+    inp = decode_inputs(w, N=len(lens))
+    inp["positions"] = lens
+    cap = 2112
+    kc, vc = decode_cache_host(w, lens, cap)
+    got = run_decode_gpu(w, inp, kc, vc, cap)
+    check_decode(w, inp, kc, vc, got)
+
+
+def test_decode_full_size_sampled_sequences():
+    # 64 sequences with caches of 1024..32768 tokens (several GB); the caches
+    # are drawn on the device with torch's seeded generator, sampled
+    # sequences are copied back and checked one by one.
+    import torch
+    w = WORKLOADS[5]
+    say(f"decode parity full size: {w.name}")
+    inp = decode_inputs(w)
+    L = inp["positions"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    kc = torch.randn((w.B, w.n_kv, w.cap, 128), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    vc = torch.randn((w.B, w.n_kv, w.cap, 128), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    y = blk.decode(dev(inp["X"], w.dtype), torch.from_numpy(L).to("cuda"), kc, vc)
+    torch.cuda.synchronize()
+    Y = host(y)
+    picks = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, 17, 42, 63})
+    for s in picks:
+        Ls = int(L[s])
+        k_all = host(kc[s, :, : Ls + 1])   # includes the new token's slot
+        v_all = host(vc[s, :, : Ls + 1])
+        sub = {k: (v[s:s + 1] if k in ("X", "positions") else v) for k, v in inp.items() if k != "lengths"}
+        ref = oracle.decode(sub["X"], sub["Wq"], sub["Wk"], sub["Wv"], sub["Wo"], sub["gq"], sub["gk"],
+                            sub["positions"], k_all[None, :, :Ls], v_all[None, :, :Ls], n_q=w.n_q,
+                            n_kv=w.n_kv, eps=EPS, theta=ROPE_THETA)
+        assert_close(Y[s:s + 1], ref["Y"], w.dtype, f"decode Y seq {s} (L={Ls})")
+        assert_close(k_all[:, Ls], ref["k_new"][0], w.dtype, f"new k seq {s}")
+    blk.close()
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+def test_decode_equals_last_prefill_row_on_gpu():
+    import torch
+    w = WORKLOADS[2]
+    T = 301
+    inp = prefill_inputs(w, B=2, T=T)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    x = dev(inp["X"], w.dtype)
+    cap = 384
+    kc = torch.zeros((2, w.n_kv, cap, 128), dtype=x.dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    y = blk.prefill(x, torch.from_numpy(inp["positions"]).to("cuda"), kc, vc)
+    kc2 = kc.clone()
+    vc2 = vc.clone()
+    kc2[:, :, T - 1:] = 0
+    vc2[:, :, T - 1:] = 0
+    yd = blk.decode(x[:, T - 1].contiguous(), torch.full((2,), T - 1, dtype=torch.int32, device="cuda"), kc2, vc2)
+    torch.cuda.synchronize()
+    assert_close(host(yd), host(y[:, T - 1]), w.dtype, "decode vs last prefill row")
+    np.testing.assert_array_equal(host(kc2[:, :, T - 1]), host(kc[:, :, T - 1]))
+    blk.close()
+
+
+# ---------------------------------------------------------------- host-side errors
+def test_forward_argument_errors():
+    import torch
+    import qwen3_gqa_attention_amd as q3
+    w = WORKLOADS[2]
+    inp = prefill_inputs(w, B=1, T=8)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    kc = torch.zeros((1, w.n_kv, 16, 128), dtype=x.dtype, device="cuda")
+    out = torch.empty_like(x)
+    need = blk.workspace_size(False, 1, 8)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    f = q3.qwen3_attn_forward_prefill
+    assert f(blk.handle, P(x), P(pos), P(kc), P(kc), 16, P(out), 1, 8, P(ws), need - 1, s) == 4
+    assert f(blk.handle, P(x), P(pos), P(kc), P(kc), 16, P(out), 1, 8, None, need, s) == 4
+    assert f(blk.handle, P(x), P(pos), P(kc), P(kc), 7, P(out), 1, 8, P(ws), need, s) == 1   # T > cap
+    assert f(blk.handle, P(x), P(pos), P(kc), P(kc), 16, P(out), 0, 8, P(ws), need, s) == 1
+    assert f(blk.handle, None, P(pos), P(kc), P(kc), 16, P(out), 1, 8, P(ws), need, s) == 1
+    assert f(blk.handle, P(x), P(pos), P(kc), P(kc), 16, P(out), 1, 8, P(ws), need, s) == 0
+    torch.cuda.synchronize()
+    blk.close()
+    # decode with an n_rep the decode kernel does not instantiate
+    w7 = dataclasses.replace(w, n_q=14, n_kv=2)
+    inp7 = prefill_inputs(w7, B=1, T=1)
+    b7 = block_from_inputs(inp7, 14, 2, "bf16")
+    with pytest.raises(q3.Qwen3AttnError) as e:
+        b7.decode(dev(inp7["X"][0], "bf16"), torch.zeros(1, dtype=torch.int32, device="cuda"),
+                  torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16, device="cuda"),
+                  torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16, device="cuda"))
+    assert e.value.status == 2
+    b7.close()

@@ -374,3 +374,14 @@ def test_inputs_are_seeded_and_reproducible():
     b = prefill_inputs(WORKLOADS[3], T=4)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_sampled_rows_equal_full_prefill():
+    p = rand_block(18, B=2, T=13)
+    full = run_prefill(p)
+    rows = [(0, 0), (1, 12), (0, 7), (1, 5)]
+    args = {k: p[k] for k in ("x", "wq", "wk", "wv", "wo", "gq", "gk", "positions")}
+    r = oracle.prefill_rows(**args, rows=rows, n_q=p["n_q"], n_kv=p["n_kv"], dh=p["dh"])
+    for i, (b, t) in enumerate(rows):
+        np.testing.assert_allclose(r["Y"][i], full["Y"][b, t], rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(r["Kc"][1], full["Kc"][1])
