@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 Qwen3 attention block on one MI355X.
+
+A step is one prefill forward of the block (q/k/v projection with fused
+QK-Norm + RoPE + cache write, causal GQA flash attention, o_proj) over the
+Qwen3-0.6B-shaped batch B=2, T=2048 (d=1024, 16 query heads, 8 KV heads,
+head dim 128, bf16 storage, fp32 accumulation) on synthetic seeded inputs
+already resident in HBM.  The decode path (64 sequences, caches of
+1024..32768 tokens) is timed beside it and reported in "decode".
+
+Prints ONE JSON line (the last line of stdout).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention-block tokens/s and TFLOP/s (% MFMA/HBM peak), 0.6B-shape B=2 T=2048"
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_flops(B, T, d, n_q, n_kv, dh=128):
+    """Algorithmic FLOPs per kernel of one prefill call."""
+    M = B * T
+    return {
+        "qkv_norm_rope_gemm": 2.0 * M * (n_q + 2 * n_kv) * dh * d,
+        "attention": 2.0 * B * n_q * dh * T * (T + 1),   # causal QK^T and PV incl. diagonal
+        "o_proj_gemm": 2.0 * M * d * n_q * dh,
+    }
+
+
+def bench_prefill(args):
+    import numpy as np
+    import torch
+
+    import qwen3_gqa_attention_amd as q3
+    from workloads import EPS, ROPE_THETA, WORKLOADS, prefill_inputs
+
+    w = WORKLOADS[2]
+    B, T = w.B, w.T
+    inp = prefill_inputs(w)
+    bf = torch.bfloat16
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(bf)
+    blk = q3.Qwen3Attention(d(inp["Wq"]), d(inp["Wk"]), d(inp["Wv"]), d(inp["Wo"]), d(inp["gq"]),
+                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA)
+    x = d(inp["X"])
+    pos = torch.from_numpy(inp["positions"]).cuda()
+    kc = torch.empty((B, w.n_kv, T, 128), dtype=bf, device="cuda")
+    vc = torch.empty_like(kc)
+    out = torch.empty_like(x)
+    ws = torch.empty(blk.workspace_size(False, B, T), dtype=torch.uint8, device="cuda")
+
+    for _ in range(args.warmup):
+        blk.prefill(x, pos, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, kernel durations from HIP events recorded by the
+    # library on the stream it launches on
+    blk.enable_stage_timing(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.prefill(x, pos, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms, ncalls = blk.stage_times()
+    blk.enable_stage_timing(0)
+
+    step_s = (t1 - t0) / args.steps
+    flops = prefill_flops(B, T, w.d, w.n_q, w.n_kv)
+    kernels = {}
+    for name, tot in zip(q3.STAGES, stage_ms):
+        avg = tot / max(ncalls, 1) / 1e3
+        kernels[name] = {"avg_ms": avg * 1e3, "gflop": flops[name] / 1e9,
+                         "tflops": flops[name] / avg / 1e12 if avg > 0 else None,
+                         "frac_mfma_peak": flops[name] / avg / PEAK_BF16_FLOPS if avg > 0 else None}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    total_flops = sum(flops.values())
+    blk.close()
+    return dict(B=B, T=T, w=w, step_s=step_s, kernels=kernels, dominant=dom, flops=flops,
+                total_flops=total_flops, ncalls=ncalls)
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    import qwen3_gqa_attention_amd as q3
+    from workloads import EPS, ROPE_THETA, WORKLOADS, decode_inputs
+
+    w = WORKLOADS[5]
+    inp = decode_inputs(w)
+    L = inp["positions"]
+    bf = torch.bfloat16
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(bf)
+    blk = q3.Qwen3Attention(d(inp["Wq"]), d(inp["Wk"]), d(inp["Wv"]), d(inp["Wo"]), d(inp["gq"]),
+                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    kc = torch.empty((w.B, w.n_kv, w.cap, 128), dtype=bf, device="cuda")
+    vc = torch.empty_like(kc)
+    for s in range(w.B):   # N(0,1) cache entries, drawn per sequence to bound the fp32 temporary
+        kc[s] = torch.randn((w.n_kv, w.cap, 128), generator=gen, device="cuda").to(bf)
+        vc[s] = torch.randn((w.n_kv, w.cap, 128), generator=gen, device="cuda").to(bf)
+    x = d(inp["X"])
+    pos = torch.from_numpy(L).cuda()
+    out = torch.empty_like(x)
+    ws = torch.empty(blk.workspace_size(True, w.B, 1, w.cap), dtype=torch.uint8, device="cuda")
+    for _ in range(max(args.warmup // 2, 2)):
+        blk.decode(x, pos, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    steps = args.decode_steps
+    blk.enable_stage_timing(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        blk.decode(x, pos, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms, ncalls = blk.stage_times()
+    blk.enable_stage_timing(0)
+    blk.close()
+    step_s = (t1 - t0) / steps
+    # algorithmic bytes: each cached key/value row read once (bf16), plus the
+    # new token's q/k/v/o weights and the small activations
+    kv_read = float(np.sum(L.astype(np.int64))) * 2 * w.n_kv * 128 * 2
+    weights = (w.n_q + 2 * w.n_kv) * 128 * w.d * 2 + w.d * w.n_q * 128 * 2
+    attn_ms = stage_ms[1] / max(ncalls, 1)
+    attn_bytes = kv_read + w.B * w.n_kv * 2 * 128 * 2 + 2 * w.B * w.n_q * 128 * 2
+    del kc, vc
+    torch.cuda.empty_cache()
+    return dict(step_s=step_s, kv_read=kv_read, weights=weights, stage_ms=[m / max(ncalls, 1) for m in stage_ms],
+                attn_ms=attn_ms, attn_bytes=attn_bytes, N=w.B, mean_len=float(L.mean()), w=w)
+
+
+def cpu_baseline(seconds):
+    """The fp64 oracle's own code run in float32 on host cores, bounded sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import EPS, ROPE_THETA, WORKLOADS, prefill_inputs
+
+    w = WORKLOADS[2]
+    T = w.T
+    inp = prefill_inputs(w, B=1, T=T)
+    args = [inp[k] for k in ("X", "Wq", "Wk", "Wv", "Wo", "gq", "gk", "positions")]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.prefill(*args, n_q=w.n_q, n_kv=w.n_kv, eps=EPS, theta=ROPE_THETA, dtype=np.float32)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": reps * T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} x oracle.prefill (float32) of one B=1,T={T} sequence of the "
+                      f"0.6B-shaped workload, {el:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the block's multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import qwen3_gqa_attention_amd as q3
+    if not os.path.exists(q3.LIB_PATH):
+        from qwen3_gqa_attention_amd.build import build
+        build()
+    torch.cuda.set_device(0)
+
+    log("bench: prefill 0.6B-shape B=2 T=2048 bf16")
+    p = bench_prefill(args)
+    log(f"bench: prefill {p['step_s'] * 1e3:.4f} ms/step; kernels " +
+        ", ".join(f"{k} {v['avg_ms']:.4f} ms" for k, v in p["kernels"].items()))
+    dec = None
+    if not args.no_decode:
+        log("bench: decode 64 sequences, caches 1024..32768")
+        dd = bench_decode(args)
+        log(f"bench: decode {dd['step_s'] * 1e3:.4f} ms/step, attention kernels {dd['attn_ms']:.4f} ms")
+        dec = {
+            "workload": dd["w"].name, "sequences": dd["N"], "mean_cache_len": dd["mean_len"],
+            "ms_per_step": dd["step_s"] * 1e3, "tokens_per_s": dd["N"] / dd["step_s"],
+            "bytes_per_step": dd["kv_read"] + dd["weights"],
+            "GBps": (dd["kv_read"] + dd["weights"]) / dd["step_s"] / 1e9,
+            "frac_hbm_peak": (dd["kv_read"] + dd["weights"]) / dd["step_s"] / PEAK_HBM_BYTES,
+            "kernel_ms": dict(zip(q3.STAGES, dd["stage_ms"])),
+            "roofline": {"bound": "hbm", "kernel": "attention (split-K + combine)",
+                         "achieved": dd["attn_bytes"] / (dd["attn_ms"] / 1e3) / 1e9,
+                         "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                         "frac": dd["attn_bytes"] / (dd["attn_ms"] / 1e3) / PEAK_HBM_BYTES,
+                         "traffic": None},
+        }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle, float32)")
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    w = p["w"]
+    dom = p["dominant"]
+    dk = p["kernels"][dom]
+    tokens = p["B"] * p["T"]
+    line = {
+        "metric": METRIC,
+        "value": tokens / p["step_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": p["step_s"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": p["B"], "T": p["T"], "d": w.d, "n_q": w.n_q,
+                   "n_kv": w.n_kv, "d_head": w.dh, "parallelism": "none (1 GPU)"},
+        "tflops": p["total_flops"] / p["step_s"] / 1e12,
+        "frac_mfma_peak": p["total_flops"] / p["step_s"] / PEAK_BF16_FLOPS,
+        "kernels": p["kernels"],
+        "roofline": {"bound": "mfma", "kernel": dom,
+                     "achieved": p["flops"][dom] / (dk["avg_ms"] / 1e3) / 1e12,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": p["flops"][dom] / (dk["avg_ms"] / 1e3) / PEAK_BF16_FLOPS,
+                     "traffic": None},
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

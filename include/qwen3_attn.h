@@ -139,6 +139,19 @@ qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,
  * enqueued work still reads it).  NULL is a no-op. */
 void qwen3_attn_destroy(qwen3_attn_t* h);
 
+/* Measurement aid.  With capacity > 0, each later forward call on this handle
+ * records a HIP event on its stream before each of its three kernels
+ * (q/k/v projection, attention, o_proj) and one after the last, for up to
+ * `capacity` calls; capacity 0 turns it off.  Not thread-safe; the handle's
+ * results are unaffected. */
+qwen3_attn_status qwen3_attn_enable_stage_timing(qwen3_attn_t* h, int32_t capacity);
+
+/* Waits for the last recorded call, then returns in ms[0..2] the summed
+ * kernel durations (ms) over the calls recorded since the previous read, and
+ * their number in *n_calls; then starts a new recording window.  `ms` is a
+ * host array of at least 3 floats. */
+qwen3_attn_status qwen3_attn_stage_times(qwen3_attn_t* h, float* ms, int32_t* n_calls);
+
 /* Static description of a status code. */
 const char* qwen3_attn_status_string(qwen3_attn_status s);
 

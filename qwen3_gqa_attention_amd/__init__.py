@@ -20,7 +20,9 @@ QWEN3_ATTN_F32 = 0
 QWEN3_ATTN_BF16 = 1
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EWORKSPACE", 5: "EHIP"}
 EXPORTED = ("qwen3_attn_create", "qwen3_attn_workspace_size", "qwen3_attn_forward_prefill",
-            "qwen3_attn_forward_decode", "qwen3_attn_destroy", "qwen3_attn_status_string")
+            "qwen3_attn_forward_decode", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
+            "qwen3_attn_stage_times", "qwen3_attn_status_string")
+STAGES = ("qkv_norm_rope_gemm", "attention", "o_proj_gemm")
 
 
 class Qwen3AttnDesc(ctypes.Structure):
@@ -63,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.qwen3_attn_forward_decode.restype = ctypes.c_int
         L.qwen3_attn_destroy.argtypes = [vp]
         L.qwen3_attn_destroy.restype = None
+        L.qwen3_attn_enable_stage_timing.argtypes = [vp, i32]
+        L.qwen3_attn_enable_stage_timing.restype = ctypes.c_int
+        L.qwen3_attn_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+        L.qwen3_attn_stage_times.restype = ctypes.c_int
         L.qwen3_attn_status_string.argtypes = [ctypes.c_int]
         L.qwen3_attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -101,6 +107,18 @@ def qwen3_attn_forward_decode(handle, hidden, positions, k_cache, v_cache, cache
 
 def qwen3_attn_destroy(handle) -> None:
     lib().qwen3_attn_destroy(handle)
+
+
+def qwen3_attn_enable_stage_timing(handle, capacity: int) -> int:
+    return lib().qwen3_attn_enable_stage_timing(handle, capacity)
+
+
+def qwen3_attn_stage_times(handle) -> tuple[int, list[float], int]:
+    """Returns (status, summed ms per kernel [3], number of calls)."""
+    ms = (ctypes.c_float * 3)()
+    n = ctypes.c_int32()
+    st = lib().qwen3_attn_stage_times(handle, ms, ctypes.byref(n))
+    return st, list(ms), n.value
 
 
 # ---------------------------------------------------------------- torch wrapper
@@ -163,6 +181,18 @@ class Qwen3Attention:
             self.close()
         except Exception:
             pass
+
+    def enable_stage_timing(self, capacity: int):
+        st = qwen3_attn_enable_stage_timing(self.handle, capacity)
+        if st != 0:
+            raise Qwen3AttnError("qwen3_attn_enable_stage_timing", st)
+
+    def stage_times(self) -> tuple[list[float], int]:
+        """Summed kernel milliseconds [qkv gemm, attention, o_proj] and the call count."""
+        st, ms, n = qwen3_attn_stage_times(self.handle)
+        if st != 0:
+            raise Qwen3AttnError("qwen3_attn_stage_times", st)
+        return ms, n
 
     def workspace_size(self, is_decode: bool, B_or_N: int, T: int = 1, cache_cap: int = 0) -> int:
         return qwen3_attn_workspace_size(self.desc, int(is_decode), B_or_N, T, cache_cap)

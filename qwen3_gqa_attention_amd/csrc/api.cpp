@@ -21,6 +21,10 @@ struct qwen3_attn {
   void* g_k;         // [128]
   float* inv_freq;   // [64] theta^(-2i/128), rounded once from double
   float inv_freq_host[64];
+  // measurement aid: events before each kernel and after the last
+  int timing_cap;
+  int timing_count;
+  hipEvent_t* events;  // [timing_cap][4]
 };
 
 namespace {
@@ -80,6 +84,29 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
   return true;
 }
 
+constexpr int kStages = 3;
+
+void mark(qwen3_attn_t* h, hipStream_t s, int i) {
+  if (h->timing_cap > 0 && h->timing_count < h->timing_cap)
+    (void)hipEventRecord(h->events[h->timing_count * (kStages + 1) + i], s);
+}
+void mark_done(qwen3_attn_t* h, hipStream_t s) {
+  if (h->timing_cap > 0 && h->timing_count < h->timing_cap) {
+    mark(h, s, kStages);
+    ++h->timing_count;
+  }
+}
+
+void free_events(qwen3_attn_t* h) {
+  if (h->events) {
+    for (int i = 0; i < h->timing_cap * (kStages + 1); ++i) (void)hipEventDestroy(h->events[i]);
+    delete[] h->events;
+  }
+  h->events = nullptr;
+  h->timing_cap = 0;
+  h->timing_count = 0;
+}
+
 qwen3_attn_status hip_status(hipError_t e) {
   return e == hipSuccess ? QWEN3_ATTN_OK : QWEN3_ATTN_EHIP;
 }
@@ -96,16 +123,20 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
                     d.n_q, d.n_kv, cap, T_len, 0, d.eps};
+  mark(h, s, 0);
   hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), M, nqkv, d.d_model,
                                         e, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  mark(h, s, 1);
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                   reinterpret_cast<const T*>(v_cache), abuf, B, T_len, d.n_q, d.n_kv,
                                   cap, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
                               M, d.d_model, hq, s);
+  mark_done(h, s);
   return hip_status(r);
 }
 
@@ -120,6 +151,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
                     d.n_q, d.n_kv, cap, 1, 1, d.eps};
+  mark(h, s, 0);
   hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), N, nqkv, d.d_model,
                                         e, s);
@@ -127,12 +159,15 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   q3::DecodeScratch sc{reinterpret_cast<float*>(ws + L.acc_off),
                        reinterpret_cast<float*>(ws + L.ml_off), L.nchunk,
                        q3::decode_chunk_keys()};
+  mark(h, s, 1);
   r = q3::launch_decode_attn<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                 reinterpret_cast<const T*>(v_cache), positions, abuf, N, d.n_q,
                                 d.n_kv, cap, sc, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
                               N, d.d_model, hq, s);
+  mark_done(h, s);
   return hip_status(r);
 }
 
@@ -261,9 +296,49 @@ void qwen3_attn_destroy(qwen3_attn_t* h) {
   const bool switched = hipGetDevice(&prev) == hipSuccess && prev != h->device &&
                         hipSetDevice(h->device) == hipSuccess;
   (void)hipDeviceSynchronize();
+  free_events(h);
   (void)hipFree(h->mem);
   if (switched) (void)hipSetDevice(prev);
   delete h;
+}
+
+qwen3_attn_status qwen3_attn_enable_stage_timing(qwen3_attn_t* h, int32_t capacity) {
+  if (!h || capacity < 0) return QWEN3_ATTN_EINVAL;
+  if (h->events) (void)hipDeviceSynchronize();
+  free_events(h);
+  if (capacity == 0) return QWEN3_ATTN_OK;
+  h->events = new (std::nothrow) hipEvent_t[(size_t)capacity * (kStages + 1)];
+  if (!h->events) return QWEN3_ATTN_ENOMEM;
+  for (int i = 0; i < capacity * (kStages + 1); ++i) {
+    if (hipEventCreate(&h->events[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(h->events[j]);
+      delete[] h->events;
+      h->events = nullptr;
+      return QWEN3_ATTN_EHIP;
+    }
+  }
+  h->timing_cap = capacity;
+  h->timing_count = 0;
+  return QWEN3_ATTN_OK;
+}
+
+qwen3_attn_status qwen3_attn_stage_times(qwen3_attn_t* h, float* ms, int32_t* n_calls) {
+  if (!h || !ms || !n_calls) return QWEN3_ATTN_EINVAL;
+  for (int j = 0; j < kStages; ++j) ms[j] = 0.f;
+  *n_calls = h->timing_count;
+  if (h->timing_count == 0) return QWEN3_ATTN_OK;
+  if (hipEventSynchronize(h->events[h->timing_count * (kStages + 1) - 1]) != hipSuccess)
+    return QWEN3_ATTN_EHIP;
+  for (int c = 0; c < h->timing_count; ++c)
+    for (int j = 0; j < kStages; ++j) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, h->events[c * (kStages + 1) + j],
+                              h->events[c * (kStages + 1) + j + 1]) != hipSuccess)
+        return QWEN3_ATTN_EHIP;
+      ms[j] += t;
+    }
+  h->timing_count = 0;
+  return QWEN3_ATTN_OK;
 }
 
 const char* qwen3_attn_status_string(qwen3_attn_status s) {
