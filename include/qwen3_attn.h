@@ -109,7 +109,8 @@ size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
  *   out       [B, T, d_model]
  * Workspace layout after the call (informative, for tests): the rotated
  * queries [B*T, n_q*d_head] then the merged attention output
- * [B*T, n_q*d_head], both of the dtype. */
+ * [B*T, n_q*d_head], both of the dtype, each padded to 256 bytes, then the
+ * RoPE (cos, sin) table [B*T, d_head/2] in fp32. */
 qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,
                                              const int32_t* positions,
                                              void* k_cache, void* v_cache,

@@ -19,8 +19,9 @@ struct qwen3_attn {
   void* w_o;         // [d, n_q * 128]
   void* g_q;         // [128]
   void* g_k;         // [128]
-  float* inv_freq;   // [64] theta^(-2i/128), rounded once from double
-  float inv_freq_host[64];
+  float* inv_freq;   // [128]: omega_i / (2 pi) as hi [0..63] + lo [64..127] floats,
+                     // omega_i = theta^(-2i/128)
+  float inv_freq_host[128];
   // measurement aid: events before each kernel and after the last
   int timing_cap;
   int timing_count;
@@ -49,7 +50,7 @@ qwen3_attn_status check_desc(const qwen3_attn_desc* d) {
 }
 
 struct WsLayout {
-  size_t q_off, a_off, acc_off, ml_off, total;
+  size_t q_off, a_off, cs_off, acc_off, ml_off, total;
   int nchunk;
 };
 
@@ -64,9 +65,10 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
     const size_t qb = align_up((size_t)n * T * hq * es);
     L->q_off = 0;
     L->a_off = qb;
+    L->cs_off = 2 * qb;
     L->acc_off = L->ml_off = 0;
     L->nchunk = 0;
-    L->total = 2 * qb;
+    L->total = L->cs_off + align_up((size_t)n * T * 64 * 2 * sizeof(float));
     return true;
   }
   if (T != 1 || cap <= 0 || cap > INT_MAX) return false;
@@ -77,7 +79,8 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
   const size_t qb = align_up((size_t)n * hq * es);
   L->q_off = 0;
   L->a_off = qb;
-  L->acc_off = 2 * qb;
+  L->cs_off = 2 * qb;
+  L->acc_off = L->cs_off + align_up((size_t)n * 64 * 2 * sizeof(float));
   L->ml_off = L->acc_off + align_up(slots * 128 * sizeof(float));
   L->total = L->ml_off + align_up(slots * 2 * sizeof(float));
   L->nchunk = (int)nchunk;
@@ -121,10 +124,13 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   const int hq = d.n_q * 128;
   T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
-  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
+  float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
+  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
                     d.n_q, d.n_kv, cap, T_len, 0, d.eps};
   mark(h, s, 0);
-  hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
+  hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, M, s);
+  if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), M, nqkv, d.d_model,
                                         e, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
@@ -149,10 +155,13 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   const int hq = d.n_q * 128;
   T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
-  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
+  float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
+  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
                     d.n_q, d.n_kv, cap, 1, 1, d.eps};
   mark(h, s, 0);
-  hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
+  hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, N, s);
+  if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), N, nqkv, d.d_model,
                                         e, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
@@ -198,7 +207,7 @@ qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc, const qwen3_att
   const size_t b_wqkv = align_up((hq + 2 * hkv) * d * es);
   const size_t b_wo = align_up(d * hq * es);
   const size_t b_g = align_up(128 * es);
-  const size_t b_f = align_up(64 * sizeof(float));
+  const size_t b_f = align_up(128 * sizeof(float));
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return QWEN3_ATTN_EHIP;
@@ -214,8 +223,12 @@ qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc, const qwen3_att
   h->g_q = p + b_wqkv + b_wo;
   h->g_k = p + b_wqkv + b_wo + b_g;
   h->inv_freq = reinterpret_cast<float*>(p + b_wqkv + b_wo + 2 * b_g);
-  for (int i = 0; i < 64; ++i)
-    h->inv_freq_host[i] = static_cast<float>(std::pow(desc->rope_theta, -2.0 * i / 128.0));
+  for (int i = 0; i < 64; ++i) {
+    const double rev = std::pow(desc->rope_theta, -2.0 * i / 128.0) / (2.0 * M_PI);
+    const float hi = static_cast<float>(rev);
+    h->inv_freq_host[i] = hi;
+    h->inv_freq_host[64 + i] = static_cast<float>(rev - static_cast<double>(hi));
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* wqkv = static_cast<char*>(h->w_qkv);
@@ -228,7 +241,7 @@ qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc, const qwen3_att
   if (r == hipSuccess) r = hipMemcpyAsync(h->g_q, w->q_norm, 128 * es, hipMemcpyDeviceToDevice, s);
   if (r == hipSuccess) r = hipMemcpyAsync(h->g_k, w->k_norm, 128 * es, hipMemcpyDeviceToDevice, s);
   if (r == hipSuccess)
-    r = hipMemcpyAsync(h->inv_freq, h->inv_freq_host, 64 * sizeof(float), hipMemcpyHostToDevice, s);
+    r = hipMemcpyAsync(h->inv_freq, h->inv_freq_host, 128 * sizeof(float), hipMemcpyHostToDevice, s);
   if (r == hipSuccess) r = hipStreamSynchronize(s);  // host staging of inv_freq must complete
   if (r != hipSuccess) {
     (void)hipFree(h->mem);

@@ -92,6 +92,21 @@ typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4_v ld16(const void* p) { return *reinterpret_cast<const u32x4_v*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4_v v) { *reinterpret_cast<u32x4_v*>(p) = v; }
 
+// Sum over the 32 lanes of each half-wave (lanes 0-31 and 32-63) with DPP
+// row permutes and one ds_swizzle; every lane of a half gets the half's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]: xor 1
+  v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]: xor 2
+  v += dpp_move<0x141>(v);  // row_half_mirror: the other quad of each 8
+  v += dpp_move<0x140>(v);  // row_mirror: the other 8 of each 16
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
+  return v;
+}
+
 // xor-butterfly reductions across lanes.
 __device__ __forceinline__ float wave_xor_sum(float v, int mask_lo, int mask_hi) {
   for (int m = mask_lo; m <= mask_hi; m <<= 1) v += __shfl_xor(v, m, kWave);

@@ -42,7 +42,7 @@ __device__ __forceinline__ int vt_pos(int k) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void flash_prefill_kernel(const T* __restrict__ Q,
+__global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restrict__ Q,
                                                             const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc,
                                                             T* __restrict__ Out, int B, int T_len,
@@ -67,7 +67,12 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(const T* __restrict_
   const int tiles_per_group = (rows_total + 127) / 128;
   const int groups = B * n_kv;
   const int bg = blockIdx.x % groups;
-  const int qt = tiles_per_group - 1 - blockIdx.x / groups;
+  // Causal balance: the first half of the grid walks query tiles from the
+  // heaviest down, the second half from the lightest up, so the two
+  // workgroups that share a CU (one from each half) carry about equal work.
+  const int rank = blockIdx.x / groups;
+  const int half = (tiles_per_group + 1) / 2;
+  const int qt = rank < half ? tiles_per_group - 1 - rank : rank - half;
   const int b = bg / n_kv, g = bg % n_kv;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -164,7 +169,8 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(const T* __restrict_
     const int buf = kt & 1;
     if (kt + 1 < ntiles) gload(kt + 1);
     if (wave_active && kt * BN <= w_tok_hi) {
-      // S^T = K Q^T
+      // S^T = K Q^T (raw scores; the 1/sqrt(d) and log2(e) scale is applied
+      // inside the exponent, and max() commutes with a positive scale)
       f32x16_v s[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -173,34 +179,39 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(const T* __restrict_
 #pragma unroll
         for (int ks = 0; ks < DSTEPS; ++ks) s[kb] = MF::run(MF::load(ks_ptr + ks * MF::K), qf[ks], s[kb]);
       }
-      // scale, causal mask, running max
-      const bool need_mask = kt * BN + BN - 1 > w_tok_lo;
+      // causal mask (only tiles that cross this wave's diagonal), running max
+      if (kt * BN + BN - 1 > w_tok_lo) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kt * BN + kb * 32 + mfma32_row(i, lane) > tok) s[kb][i] = -INFINITY;
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[kb][i] * scale_log2;
-          if (need_mask && kt * BN + kb * 32 + mfma32_row(i, lane) > tok) x = -INFINITY;
-          s[kb][i] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[kb][i]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * scale_log2;
+      // Rescale the running sum and O only if some lane's max rose.
+      if (__ballot(mloc > m_run) != 0) {
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      }
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(s[kb][i] - m_new);
+          const float p = exp2f(fmaf(s[kb][i], scale_log2, -m_run));
           s[kb][i] = p;
           lsum += p;
         }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      l_run += lsum;
 
       // O^T += V^T P^T
       if constexpr (VT) {

@@ -5,17 +5,28 @@
 // layout of the token-major activations, so every MFMA operand fragment is a
 // contiguous 16-byte run along K.
 //
-// Tile: BM x 128 x BK, BK = 128 bytes of K per row.  The 128-wide N tile is
-// exactly one head of d_head = 128, so the q/k epilogue sees a whole head:
-// the per-head RMSNorm and the RoPE pairing of column c with c + 64 stay
-// inside one wavefront.  Each wave owns 32*MI rows and all 128 columns
-// (4 MFMA 32x32 blocks): with the 32x32 accumulator layout a lane holds
-// columns c, c+32, c+64, c+96 of its rows, so RoPE is lane-local and the
-// sum of squares is a 32-lane butterfly.
+// Workgroup tile BM x BN x BK (BK = 128 bytes of K per row), WM x WN waves,
+// each wave owning (32*MI) x (32*NI) outputs as MI x NI accumulators of the
+// 32x32 MFMA.  Large wave tiles keep LDS traffic per MFMA low: a 128x128 wave
+// tile reads 8 fragments (8 KB) from LDS per 16 MFMAs.
 //
-// Staging: global -> VGPR (16-byte loads) -> LDS (double buffer, rows padded
-// by 16 bytes so ds_read_b128 of 16 consecutive rows hits distinct banks),
-// with the next k-tile's global loads in flight during the current MFMAs.
+// For the q/k/v projection NI = 4: a wave's 128 columns are exactly one head
+// of d_head = 128, so the epilogue sees whole heads.  With the 32x32
+// accumulator layout a lane holds columns c, c+32, c+64, c+96 of its rows:
+// the RoPE pair (c, c+64) is lane-local and the head's sum of squares is a
+// 32-lane DPP/swizzle reduction.  cos/sin come from a per-call table
+// (rope_table_kernel): one evaluation per (token, frequency) instead of one
+// per (token, frequency, head).
+//
+// Staging: global -> VGPR (16-byte loads) -> LDS, double buffered.  LDS rows
+// are 128 bytes, unpadded, with the 16-byte chunk c of row r stored at chunk
+// c ^ ((r >> 1) & 7): the 16-byte writes of 8 lanes per row and the
+// 16-byte fragment reads of 16 consecutive rows both hit distinct banks.  The
+// next k-tile's global loads are in flight during the current tile's MFMAs.
+// Results leave through LDS as well, so every global store is 16 bytes of a
+// row.  Workgroups are mapped so that each XCD (workgroups are dealt
+// round-robin over the 8 XCDs) works on a compact block of tiles, which keeps
+// the operands it shares in its own L2.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -26,42 +37,108 @@ struct StoreEpilogue {
   int ldc;
 };
 
-template <typename T, int WM, int MI, bool QKV>
-__global__ __launch_bounds__(WM * 64) void gemm_nt_kernel(const T* __restrict__ A,
-                                                           const T* __restrict__ B, int M,
-                                                           int N, int K, QkvEpilogue qe,
-                                                           StoreEpilogue se) {
+constexpr int kXcds = 8;
+
+// sin and cos of the RoPE angle p * omega for an integer position p, with
+// omega / (2 pi) given as hi + lo floats.  The angle is reduced in
+// revolutions exactly -- p * hi is split into its rounded value and its
+// rounding error with one fma, and fract() of a float is exact -- so the
+// hardware sin/cos (which take revolutions) see an argument in [0, 1)
+// accurate to about 2^-24 revolutions at any position.
+__device__ __forceinline__ void rope_sincos(int pos, float whi, float wlo, float* s, float* c) {
+  const float p = static_cast<float>(pos);
+  const float r = p * whi;
+  const float e = fmaf(p, whi, -r) + p * wlo;
+  const float f = __builtin_amdgcn_fractf(__builtin_amdgcn_fractf(r) + e);
+  *s = __builtin_amdgcn_sinf(f);
+  *c = __builtin_amdgcn_cosf(f);
+}
+
+// cs[row][i] = (cos, sin) of positions[row] * omega_i, i < 64.
+__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restrict__ positions,
+                                                         const float* __restrict__ inv_freq,
+                                                         float2* __restrict__ cs, int M) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * 64) return;
+  const int row = idx >> 6, i = idx & 63;
+  float s, c;
+  rope_sincos(positions[row], inv_freq[i], inv_freq[64 + i], &s, &c);
+  cs[idx] = make_float2(c, s);
+}
+
+hipError_t launch_rope_table(const int32_t* positions, const float* inv_freq, float2* cs, int M,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3((M * 64 + 255) / 256), dim3(256), 0, s, positions,
+                     inv_freq, cs, M);
+  return hipGetLastError();
+}
+
+// Linear workgroup id -> (m tile, n tile): XCD x gets the contiguous range
+// [x*per, (x+1)*per) of a walk over GN-wide column groups (m slower, n
+// faster inside a group).
+__device__ __forceinline__ void tile_of_block(int bid, int mt, int nt, int* tm, int* tn) {
+  const int total = mt * nt;
+  int t = bid;
+  if (total % kXcds == 0) {
+    const int per = total / kXcds;
+    t = (bid % kXcds) * per + bid / kXcds;
+  }
+  constexpr int GN = 4;
+  const int group = t / (GN * mt);
+  const int first_n = group * GN;
+  const int gw = min(GN, nt - first_n);
+  const int r = t - group * GN * mt;
+  *tm = r / gw;
+  *tn = first_n + r % gw;
+}
+
+// Element offset of (row, k) in a swizzled 128-byte-row LDS tile.
+template <int EPC>
+__device__ __forceinline__ int swz(int row, int k) {
+  return row * (8 * EPC) + ((((k / EPC) ^ (row >> 1)) & 7) * EPC) + (k % EPC);
+}
+
+template <typename T, int WM, int WN, int MI, int NI, bool QKV>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restrict__ A,
+                                                                const T* __restrict__ B, int M,
+                                                                int N, int K, QkvEpilogue qe,
+                                                                StoreEpilogue se) {
   using MF = Mfma32<T>;
-  constexpr int NT = WM * 64;
+  constexpr int NT = WM * WN * 64;
   constexpr int BM = 32 * MI * WM;
-  constexpr int BN = 128;
+  constexpr int BN = 32 * NI * WN;
   constexpr int EPC = 16 / sizeof(T);    // elements per 16-byte chunk
-  constexpr int BK = 8 * EPC;            // 128 bytes of K per row per k-tile
-  constexpr int LDK = BK + EPC;          // padded LDS row (elements)
+  constexpr int BK = 8 * EPC;            // 128 bytes of K per row
   constexpr int A_CH = BM * 8 / NT;      // 16-byte chunks per thread per k-tile
   constexpr int B_CH = BN * 8 / NT;
+  constexpr int KS = BK / MF::K;         // MFMA k-steps per k-tile
+  constexpr int STAGE = (BM + BN) * BK;  // elements per LDS stage
+  // epilogue staging (bf16 only; fp32 results are stored from registers)
+  constexpr int STAGED = sizeof(T) == 2 ? (NT / 64) * (32 * MI) * (32 * NI + 8) : 0;
+  constexpr int SMEM = 2 * STAGE > STAGED ? 2 * STAGE : STAGED;
   static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads mismatch");
+  static_assert(!QKV || NI == 4, "q/k/v epilogue needs one whole head per wave");
 
-  __shared__ __attribute__((aligned(16))) T As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) T Bs[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
   const int c32 = lane & 31;
   const int hk = lane >> 5;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
+  int tm, tn;
+  tile_of_block(blockIdx.x, (M + BM - 1) / BM, N / BN, &tm, &tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
 
   u32x4_v ra[A_CH], rb[B_CH];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT, r = c >> 3, cc = c & 7;
-      if (m0 + r < M)
-        ra[i] = ld16(A + (size_t)(m0 + r) * K + k0 + cc * EPC);
-      else
-        ra[i] = u32x4_v{0u, 0u, 0u, 0u};
+      const int row = min(m0 + r, M - 1);  // rows past M load a valid row; never stored
+      ra[i] = ld16(A + (size_t)row * K + k0 + cc * EPC);
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
@@ -70,146 +147,185 @@ __global__ __launch_bounds__(WM * 64) void gemm_nt_kernel(const T* __restrict__ 
     }
   };
   auto sstore = [&](int buf) {
+    T* as = smem + buf * STAGE;
+    T* bs = as + BM * BK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT, r = c >> 3, cc = c & 7;
-      st16(&As[buf][r * LDK + cc * EPC], ra[i]);
+      st16(as + swz<EPC>(r, cc * EPC), ra[i]);
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int c = tid + i * NT, r = c >> 3, cc = c & 7;
-      st16(&Bs[buf][r * LDK + cc * EPC], rb[i]);
+      st16(bs + swz<EPC>(r, cc * EPC), rb[i]);
     }
   };
 
-  f32x16_v acc[MI][4];
+  f32x16_v acc[MI][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16_v{};
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_v{};
 
   const int KT = K / BK;
+  const int arow = wm * 32 * MI + c32;   // this lane's first A row in the tile
+  const int brow = wn * 32 * NI + c32;   // this lane's first B row in the tile
   gload(0);
   sstore(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < KT) gload((kt + 1) * BK);
-    const T* as = &As[buf][(wave * 32 * MI + c32) * LDK + hk * MF::KL];
-    const T* bs = &Bs[buf][c32 * LDK + hk * MF::KL];
+    const T* as = smem + buf * STAGE;
+    const T* bs = as + BM * BK;
 #pragma unroll
-    for (int ks = 0; ks < BK / MF::K; ++ks) {
-      typename MF::frag af[MI], bfr[4];
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k = ks * MF::K + hk * MF::KL;
+      typename MF::frag af[MI], bfr[NI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[mi] = MF::load(as + mi * 32 * LDK + ks * MF::K);
+      for (int mi = 0; mi < MI; ++mi) af[mi] = MF::load(as + swz<EPC>(arow + mi * 32, k));
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) bfr[ni] = MF::load(bs + ni * 32 * LDK + ks * MF::K);
+      for (int ni = 0; ni < NI; ++ni) bfr[ni] = MF::load(bs + swz<EPC>(brow + ni * 32, k));
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = MF::run(af[mi], bfr[ni], acc[mi][ni]);
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = MF::run(af[mi], bfr[ni], acc[mi][ni]);
     }
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
 
   // ------------------------------------------------------------------ epilogue
-  if constexpr (!QKV) {
-    T* C = reinterpret_cast<T*>(se.c);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = m0 + wave * 32 * MI + mi * 32 + mfma32_row(i, lane);
-        if (row < M) {
-          T* dst = C + (size_t)row * se.ldc + n0 + c32;
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) dst[ni * 32] = from_f32<T>(acc[mi][ni][i]);
-        }
-      }
-  } else {
-    // Head index of this N tile: [0, n_q) query heads, then n_kv key heads,
-    // then n_kv value heads.
-    const int head = blockIdx.x;
-    const int kind = head < qe.n_q ? 0 : (head < qe.n_q + qe.n_kv ? 1 : 2);
-    float gain[4] = {1.f, 1.f, 1.f, 1.f};
-    float w0 = 0.f, w1 = 0.f;
+  const int row_base = m0 + wm * 32 * MI;
+  int head = 0, kind = 3;  // kind 3: plain projection output
+  if constexpr (QKV) {
+    // This wave's 128 columns are head (n0/128 + wn): [0, n_q) query heads,
+    // then n_kv key heads, then n_kv value heads.
+    head = (n0 >> 7) + wn;
+    kind = head < qe.n_q ? 0 : (head < qe.n_q + qe.n_kv ? 1 : 2);
     if (kind != 2) {
+      float gain[4];
       const T* g = reinterpret_cast<const T*>(kind == 0 ? qe.gq : qe.gk);
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) gain[ni] = to_f32<T>(g[ni * 32 + c32]);
-      w0 = qe.inv_freq[c32];
-      w1 = qe.inv_freq[32 + c32];
-    }
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) {
+        float2 cs0[16], cs1[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = m0 + wave * 32 * MI + mi * 32 + mfma32_row(i, lane);
-        const bool ok = row < M;
-        float v0 = acc[mi][0][i], v1 = acc[mi][1][i], v2 = acc[mi][2][i], v3 = acc[mi][3][i];
-        const int pos = ok ? qe.positions[row] : 0;
-        if (kind != 2) {
+        for (int i = 0; i < 16; ++i) {
+          const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
+          cs0[i] = qe.rope_cs[(size_t)row * 64 + c32];
+          cs1[i] = qe.rope_cs[(size_t)row * 64 + 32 + c32];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v0 = acc[mi][0][i], v1 = acc[mi][1][i], v2 = acc[mi][2][i], v3 = acc[mi][3][i];
           // RMS over the head's 128 columns: 4 per lane, 32 lanes per half-wave.
-          float ss = v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
-          ss = wave_xor_sum(ss, 1, 16);
+          const float ss = half_wave_sum(v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3);
           const float rs = rsqrtf(ss * (1.f / 128.f) + qe.eps);
           v0 *= rs * gain[0];
           v1 *= rs * gain[1];
           v2 *= rs * gain[2];
           v3 *= rs * gain[3];
           // RoPE: column c pairs with c + 64 (lane-local: blocks 0/2 and 1/3).
-          float s0, c0, s1, c1;
-          sincosf(static_cast<float>(pos) * w0, &s0, &c0);
-          sincosf(static_cast<float>(pos) * w1, &s1, &c1);
-          const float r0 = v0 * c0 - v2 * s0, r2 = v2 * c0 + v0 * s0;
-          const float r1 = v1 * c1 - v3 * s1, r3 = v3 * c1 + v1 * s1;
-          v0 = r0; v1 = r1; v2 = r2; v3 = r3;
+          acc[mi][0][i] = v0 * cs0[i].x - v2 * cs0[i].y;
+          acc[mi][2][i] = v2 * cs0[i].x + v0 * cs0[i].y;
+          acc[mi][1][i] = v1 * cs1[i].x - v3 * cs1[i].y;
+          acc[mi][3][i] = v3 * cs1[i].x + v1 * cs1[i].y;
         }
-        if (!ok) continue;
-        T* dst;
-        if (kind == 0) {
-          dst = reinterpret_cast<T*>(qe.q_out) + (size_t)row * (qe.n_q * kHeadDim) +
-                head * kHeadDim;
-        } else {
-          const int g = head - qe.n_q - (kind == 2 ? qe.n_kv : 0);
-          const int seq = qe.decode ? row : row / qe.rows_per_seq;
-          const int slot = qe.decode ? pos : row % qe.rows_per_seq;
-          T* cache = reinterpret_cast<T*>(kind == 1 ? qe.k_cache : qe.v_cache);
-          dst = cache + ((size_t)(seq * qe.n_kv + g) * qe.cap + slot) * kHeadDim;
+      }
+    }
+  }
+
+  // Destination of row `row`, columns [col0, col0 + 32*NI) of this wave.
+  auto dst_row = [&](int row) -> T* {
+    if constexpr (!QKV) {
+      return reinterpret_cast<T*>(se.c) + (size_t)row * se.ldc + n0 + wn * 32 * NI;
+    } else {
+      if (kind == 0)
+        return reinterpret_cast<T*>(qe.q_out) + (size_t)row * (qe.n_q * kHeadDim) + head * kHeadDim;
+      const int g = head - qe.n_q - (kind == 2 ? qe.n_kv : 0);
+      const int seq = qe.decode ? row : row / qe.rows_per_seq;
+      const int slot = qe.decode ? qe.positions[row] : row % qe.rows_per_seq;
+      T* cache = reinterpret_cast<T*>(kind == 1 ? qe.k_cache : qe.v_cache);
+      return cache + ((size_t)(seq * qe.n_kv + g) * qe.cap + slot) * kHeadDim;
+    }
+  };
+
+  if constexpr (sizeof(T) == 2) {
+    // Stage the wave's (32*MI) x (32*NI) bf16 block in LDS (rows padded by 16
+    // bytes), then write whole 16-byte pieces of rows to global memory.
+    constexpr int WCOLS = 32 * NI;
+    constexpr int LDW = WCOLS + 8;
+    constexpr int CPR = WCOLS / 8;        // 16-byte chunks per row
+    static_assert(NT / 64 * (32 * MI) * LDW <= SMEM, "staging does not fit");
+    T* st = smem + wave * (32 * MI) * LDW;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = mi * 32 + mfma32_row(i, lane);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) st[r * LDW + ni * 32 + c32] = from_f32<T>(acc[mi][ni][i]);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    constexpr int RPI = 64 / CPR;         // rows per wave instruction
+#pragma unroll 4
+    for (int r0 = 0; r0 < 32 * MI; r0 += RPI) {
+      const int r = r0 + lane / CPR, ch = lane % CPR;
+      const int row = row_base + r;
+      if (row < M) st16(dst_row(row) + ch * 8, ld16(st + r * LDW + ch * 8));
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = row_base + mi * 32 + mfma32_row(i, lane);
+        if (row < M) {
+          T* dst = dst_row(row) + c32;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) dst[ni * 32] = acc[mi][ni][i];
         }
-        dst[c32] = from_f32<T>(v0);
-        dst[32 + c32] = from_f32<T>(v1);
-        dst[64 + c32] = from_f32<T>(v2);
-        dst[96 + c32] = from_f32<T>(v3);
       }
   }
 }
 
-template <typename T, int WM, int MI, bool QKV>
+template <typename T, int WM, int WN, int MI, int NI, bool QKV>
 static hipError_t launch_gemm(const T* A, const T* B, int M, int N, int K, const QkvEpilogue& qe,
                               const StoreEpilogue& se, hipStream_t s) {
   constexpr int BM = 32 * MI * WM;
-  dim3 grid(N / 128, (M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, MI, QKV>), grid, dim3(WM * 64), 0, s, A, B, M, N, K,
-                     qe, se);
+  constexpr int BN = 32 * NI * WN;
+  const int tiles = ((M + BM - 1) / BM) * (N / BN);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV>), dim3(tiles), dim3(WM * WN * 64), 0,
+                     s, A, B, M, N, K, qe, se);
   return hipGetLastError();
 }
 
+constexpr int kCus = 256;
+
+// Tile choice.  Large problems: 256x256 tiles of 8 waves (64x128 each, two
+// waves per SIMD so one wave's MFMAs cover the other's LDS and barrier
+// waits).  Mid-size: 128x128 tiles.  Decode-sized M <= 64: 64x128 tiles.
 template <typename T>
 hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const QkvEpilogue& e,
                            hipStream_t s) {
   StoreEpilogue se{nullptr, 0};
-  if (M <= 64) return launch_gemm<T, 2, 1, true>(X, Wqkv, M, N, K, e, se, s);
-  return launch_gemm<T, 4, 1, true>(X, Wqkv, M, N, K, e, se, s);
+  if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
+  if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus)
+    return launch_gemm<T, 4, 2, 2, 4, true>(X, Wqkv, M, N, K, e, se, s);
+  return launch_gemm<T, 4, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
 }
 
 template <typename T>
 hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, hipStream_t s) {
   QkvEpilogue qe{};
   StoreEpilogue se{C, N};
-  if (M <= 64) return launch_gemm<T, 2, 1, false>(A, W, M, N, K, qe, se, s);
-  return launch_gemm<T, 4, 1, false>(A, W, M, N, K, qe, se, s);
+  if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, false>(A, W, M, N, K, qe, se, s);
+  if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus)
+    return launch_gemm<T, 4, 2, 2, 4, false>(A, W, M, N, K, qe, se, s);
+  return launch_gemm<T, 2, 2, 2, 2, false>(A, W, M, N, K, qe, se, s);
 }
 
 template hipError_t launch_qkv_gemm<float>(const float*, const float*, int, int, int,

@@ -14,16 +14,21 @@ struct QkvEpilogue {
   void* q_out;               // [rows, n_q*128]
   void* k_cache;             // [seqs, n_kv, cap, 128]
   void* v_cache;             // [seqs, n_kv, cap, 128]
-  const int32_t* positions;  // [rows] RoPE position of each row
+  const int32_t* positions;  // [rows] position of each row (decode: its cache slot)
   const void* gq;            // [128] q_norm gain (dtype of the block)
   const void* gk;            // [128] k_norm gain
-  const float* inv_freq;     // [64] theta^(-2i/128)
+  const float2* rope_cs;     // [rows][64] (cos, sin) of position * omega_i
   int n_q, n_kv;
   int64_t cap;
   int rows_per_seq;          // prefill: T (slot = row % T); decode: 1
   int decode;                // 1: cache slot = positions[row]
   float eps;
 };
+
+// cs[row][i] = (cos, sin)(positions[row] * omega_i), i < 64, with omega_i / (2 pi)
+// given as hi [0..63] + lo [64..127] floats in inv_freq.
+hipError_t launch_rope_table(const int32_t* positions, const float* inv_freq, float2* cs, int M,
+                             hipStream_t s);
 
 // q/k/v projection X[M,K] * Wqkv[N,K]^T with the fused epilogue; N = (n_q + 2 n_kv) * 128.
 template <typename T>

@@ -71,14 +71,15 @@ def align(x):
 
 def test_workspace_size_prefill_and_decode(built_lib):
     d = desc()
-    assert q3.qwen3_attn_workspace_size(d, 0, 2, 2048, 0) == 2 * align(2 * 2048 * 2048 * 2)
+    # prefill: rotated q, merged attention output, RoPE (cos, sin) table
+    assert q3.qwen3_attn_workspace_size(d, 0, 2, 2048, 0) == 2 * align(2 * 2048 * 2048 * 2) + align(4096 * 64 * 8)
     d32 = desc(dtype=q3.QWEN3_ATTN_F32)
-    assert q3.qwen3_attn_workspace_size(d32, 0, 1, 128, 0) == 2 * align(128 * 2048 * 4)
+    assert q3.qwen3_attn_workspace_size(d32, 0, 1, 128, 0) == 2 * align(128 * 2048 * 4) + align(128 * 64 * 8)
     # decode: q and merged output, then per-chunk partials (512-key chunks)
     cap, N = 32832, 64
     nchunk = -(-cap // 512)
     slots = N * 8 * nchunk * 2
-    want = 2 * align(N * 2048 * 2) + align(slots * 128 * 4) + align(slots * 2 * 4)
+    want = 2 * align(N * 2048 * 2) + align(N * 64 * 8) + align(slots * 128 * 4) + align(slots * 2 * 4)
     assert q3.qwen3_attn_workspace_size(d, 1, N, 1, cap) == want
 
 
