@@ -11,6 +11,7 @@ namespace q3 {
 typedef uint16_t bf16_t;  // bf16 bit pattern in memory
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef float f32x16_v __attribute__((ext_vector_type(16)));
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
 
@@ -34,6 +35,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// acc + lo + hi of a packed bf16 pair (one v_dot2 with (1, 1)).
+__device__ __forceinline__ float sum2_bf16(uint32_t packed, float acc) {
+  const uint32_t ones = 0x3f803f80u;
+  bf16x2_v a, b;
+  __builtin_memcpy(&a, &packed, 4);
+  __builtin_memcpy(&b, &ones, 4);
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }

@@ -102,21 +102,31 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
   const T* Vg = Vc + (size_t)(b * n_kv + g) * cap * kHeadDim;
 
   u32x4_v rk[KCH], rv[KCH];
+  // Per-thread K/V row pointers for tile 0; each tile advances them by BN rows.
+  // bf16: K rows (tid >> 4) + 16 i, chunk tid & 15; V keys 4 (tid & 15) + d,
+  // dims 8 (tid >> 4) .. + 7 (the thread owns 4 consecutive keys x 8 dims).
+  const int k_row0 = VT ? (tid >> 4) : 0;
+  const int v_key0 = VT ? (tid & 15) * 4 : 0;
+  const T* kp = Kg + (size_t)k_row0 * kHeadDim + (VT ? (tid & 15) * EPC : 0);
+  const T* vp0 = Vg + (size_t)v_key0 * kHeadDim + (VT ? (tid >> 4) * 8 : 0);
   auto gload = [&](int kt) {
     const int kbase = kt * BN;
     if constexpr (VT) {
-      // K: 16 chunks per key row.  V: thread owns 4 consecutive keys x 8 dims.
+      const T* kpt = kp + (size_t)kbase * kHeadDim;
+      const T* vpt = vp0 + (size_t)kbase * kHeadDim;
+      if (kbase + BN <= T_len) {
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int c = tid + i * 256, key = c >> 4, cc = c & 15;
-        rk[i] = (kbase + key < T_len) ? ld16(Kg + (size_t)(kbase + key) * kHeadDim + cc * EPC)
-                                      : u32x4_v{0u, 0u, 0u, 0u};
-      }
-      const int quad = tid & 15, oct = tid >> 4;
+        for (int i = 0; i < KCH; ++i) rk[i] = ld16(kpt + (size_t)i * 16 * kHeadDim);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int key = kbase + quad * 4 + d;
-        rv[d] = key < T_len ? ld16(Vg + (size_t)key * kHeadDim + oct * 8) : u32x4_v{0u, 0u, 0u, 0u};
+        for (int d = 0; d < 4; ++d) rv[d] = ld16(vpt + (size_t)d * kHeadDim);
+      } else {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i)
+          rk[i] = (kbase + k_row0 + 16 * i < T_len) ? ld16(kpt + (size_t)i * 16 * kHeadDim)
+                                                    : u32x4_v{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          rv[d] = (kbase + v_key0 + d < T_len) ? ld16(vpt + (size_t)d * kHeadDim) : u32x4_v{0u, 0u, 0u, 0u};
       }
     } else {
 #pragma unroll
@@ -202,32 +212,41 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
       }
-      float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(fmaf(s[kb][i], scale_log2, -m_run));
-          s[kb][i] = p;
-          lsum += p;
-        }
-      l_run += lsum;
+        for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], scale_log2, -m_run));
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T.  The running sum adds the bf16-rounded P that the
+      // MFMA consumes, two at a time (dot2 with ones).
       if constexpr (VT) {
+        float lsum = 0.f;
 #pragma unroll
         for (int ks2 = 0; ks2 < BN / 16; ++ks2) {
           const int kb = ks2 >> 1, i0 = (ks2 & 1) * 8;
-          u32x4_v pw{pack_bf16x2(s[kb][i0 + 0], s[kb][i0 + 1]), pack_bf16x2(s[kb][i0 + 2], s[kb][i0 + 3]),
-                     pack_bf16x2(s[kb][i0 + 4], s[kb][i0 + 5]), pack_bf16x2(s[kb][i0 + 6], s[kb][i0 + 7])};
-          const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, pw);
+          const uint32_t w0 = pack_bf16x2(s[kb][i0 + 0], s[kb][i0 + 1]);
+          const uint32_t w1 = pack_bf16x2(s[kb][i0 + 2], s[kb][i0 + 3]);
+          const uint32_t w2 = pack_bf16x2(s[kb][i0 + 4], s[kb][i0 + 5]);
+          const uint32_t w3 = pack_bf16x2(s[kb][i0 + 6], s[kb][i0 + 7]);
+          lsum = sum2_bf16(w0, lsum);
+          lsum = sum2_bf16(w1, lsum);
+          lsum = sum2_bf16(w2, lsum);
+          lsum = sum2_bf16(w3, lsum);
+          const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, u32x4_v{w0, w1, w2, w3});
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
             const T* vp = &Vs[buf][(db * 32 + c32) * LDV + ks2 * 16 + hk * 8];
             o[db] = MF::run(MF::load(vp), pf, o[db]);
           }
         }
+        l_run += lsum;
       } else {
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) lsum += s[kb][i];
+        l_run += lsum;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
