@@ -29,9 +29,11 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   __bf16 b = static_cast<__bf16>(f);
   return __builtin_bit_cast(bf16_t, b);
 }
-// Two f32 -> packed bf16x2 (lo = a, hi = b).
+// Two f32 -> packed bf16x2 (lo = a, hi = b), one v_cvt_pk_bf16_f32.
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cv __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, bf16x2_cv));
 }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -101,6 +103,16 @@ typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x4_v ld16(const void* p) { return *reinterpret_cast<const u32x4_v*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4_v v) { *reinterpret_cast<u32x4_v*>(p) = v; }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load (a workgroup fence on all memory), which
+// would drain loads prefetched for later tiles; this one leaves them in
+// flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Sum over the 32 lanes of each half-wave (lanes 0-31 and 32-63) with DPP
 // row permutes and one ds_swizzle; every lane of a half gets the half's sum.

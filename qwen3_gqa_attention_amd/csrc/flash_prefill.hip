@@ -8,11 +8,15 @@
 // max and sum (the online softmax that "Qwen3 Architecture Layer-by-Layer"
 // names in its cross-entropy section).
 //
-// Work decomposition.  One workgroup (4 waves) owns 128 "packed rows" of one
+// Work decomposition.  One workgroup owns 128 "packed rows" of one
 // (sequence, KV head): row R stands for token R / n_rep and query head
 // g*n_rep + R % n_rep, so the n_rep query heads that share a KV head share
-// every K/V tile staged in LDS; the KV heads are never copied.  Each wave owns
-// 32 rows.  Workgroups are issued heaviest (longest key range) first.
+// every K/V tile staged in LDS; the KV heads are never copied.  The workgroup
+// has 8 waves: 4 query blocks of 32 rows times 2 halves of the key range,
+// merged at the end (the same log-sum-exp merge as split-K decode).  The two
+// waves that share a SIMD thus work on the same query tile for its whole
+// duration, which halves its critical path.  Workgroups are issued heaviest
+// (longest key range) first.
 //
 // Per wave and 64-key tile (bf16):
 //   S^T[key, q] = K . Q^T    -- A = K rows from LDS, B = Q^T held in VGPRs;
@@ -41,8 +45,8 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restrict__ Q,
+template <typename T, int KSPLIT>
+__global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T* __restrict__ Q,
                                                             const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc,
                                                             T* __restrict__ Out, int B, int T_len,
@@ -59,27 +63,34 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
   constexpr int KCH = BN * (kHeadDim / EPC) / 256;  // K chunks per thread per tile
   constexpr int DSTEPS = kHeadDim / MF::K;     // MFMA steps over d_head
 
-  __shared__ __attribute__((aligned(16))) T Ks[2][BN * LDK];
-  __shared__ __attribute__((aligned(16))) T Vs[2][VSZ];
+  // Two key halves x two stages of K and V tiles; after the key loop the
+  // same memory carries the second half's partial results to the first.
+  constexpr int KSZ = BN * LDK;
+  constexpr int COMB = 4 * 66 * 64 * 4 / sizeof(T);   // 4 blocks x (64 O + m + l) x 64 lanes, fp32
+  constexpr int SMEM = 2 * KSPLIT * (KSZ + VSZ) > COMB ? 2 * KSPLIT * (KSZ + VSZ) : COMB;
+  __shared__ __attribute__((aligned(16))) T smem[SMEM];
+  auto Ks = [&](int st) { return smem + st * KSZ; };
+  auto Vs = [&](int st) { return smem + 2 * KSPLIT * KSZ + st * VSZ; };
 
   const int n_rep = n_q / n_kv;
   const int rows_total = T_len * n_rep;
   const int tiles_per_group = (rows_total + 127) / 128;
   const int groups = B * n_kv;
   const int bg = blockIdx.x % groups;
-  // Causal balance: the first half of the grid walks query tiles from the
-  // heaviest down, the second half from the lightest up, so the two
-  // workgroups that share a CU (one from each half) carry about equal work.
-  const int rank = blockIdx.x / groups;
-  const int half = (tiles_per_group + 1) / 2;
-  const int qt = rank < half ? tiles_per_group - 1 - rank : rank - half;
+  // Query tiles are issued heaviest (longest key range) first, so lighter
+  // ones fill CUs as they free up.
+  const int qt = tiles_per_group - 1 - blockIdx.x / groups;
   const int b = bg / n_kv, g = bg % n_kv;
 
+  // Wave w owns query block w & 3 (32 rows) over key half w >> 2 (with
+  // KSPLIT = 2; with KSPLIT = 1 four waves cover the whole key range).
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qblk = wave & 3, kh = KSPLIT == 2 ? (wave >> 2) : 0;
+  const int th = tid & 255;                    // thread index inside the key half
   const int c32 = lane & 31, hk = lane >> 5;
 
   const int R0 = qt * 128;
-  const int Rw = R0 + wave * 32;
+  const int Rw = R0 + qblk * 32;
   const int Rl = Rw + c32;
   const bool row_ok = Rl < rows_total;
   const int tok = row_ok ? Rl / n_rep : T_len - 1;
@@ -101,15 +112,15 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
   const T* Kg = Kc + (size_t)(b * n_kv + g) * cap * kHeadDim;
   const T* Vg = Vc + (size_t)(b * n_kv + g) * cap * kHeadDim;
 
-  u32x4_v rk[KCH], rv[KCH];
+  u32x4_v rkA[KCH], rvA[KCH], rkB[KCH], rvB[KCH];
   // Per-thread K/V row pointers for tile 0; each tile advances them by BN rows.
   // bf16: K rows (tid >> 4) + 16 i, chunk tid & 15; V keys 4 (tid & 15) + d,
   // dims 8 (tid >> 4) .. + 7 (the thread owns 4 consecutive keys x 8 dims).
-  const int k_row0 = VT ? (tid >> 4) : 0;
-  const int v_key0 = VT ? (tid & 15) * 4 : 0;
-  const T* kp = Kg + (size_t)k_row0 * kHeadDim + (VT ? (tid & 15) * EPC : 0);
-  const T* vp0 = Vg + (size_t)v_key0 * kHeadDim + (VT ? (tid >> 4) * 8 : 0);
-  auto gload = [&](int kt) {
+  const int k_row0 = VT ? (th >> 4) : 0;
+  const int v_key0 = VT ? (th & 15) * 4 : 0;
+  const T* kp = Kg + (size_t)k_row0 * kHeadDim + (VT ? (th & 15) * EPC : 0);
+  const T* vp0 = Vg + (size_t)v_key0 * kHeadDim + (VT ? (th >> 4) * 8 : 0);
+  auto gload = [&](int kt, u32x4_v (&rk)[KCH], u32x4_v (&rv)[KCH]) {
     const int kbase = kt * BN;
     if constexpr (VT) {
       const T* kpt = kp + (size_t)kbase * kHeadDim;
@@ -131,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
     } else {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
-        const int c = tid + i * 256, key = c >> 5, cc = c & 31;
+        const int c = th + i * 256, key = c >> 5, cc = c & 31;
         const size_t off = (size_t)(kbase + key) * kHeadDim + cc * EPC;
         const bool ok = kbase + key < T_len;
         rk[i] = ok ? ld16(Kg + off) : u32x4_v{0u, 0u, 0u, 0u};
@@ -139,14 +150,14 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const u32x4_v (&rk)[KCH], const u32x4_v (&rv)[KCH]) {
     if constexpr (VT) {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
-        const int c = tid + i * 256, key = c >> 4, cc = c & 15;
-        st16(&Ks[buf][key * LDK + cc * EPC], rk[i]);
+        const int c = th + i * 256, key = c >> 4, cc = c & 15;
+        st16(Ks(buf) + key * LDK + cc * EPC, rk[i]);
       }
-      const int quad = tid & 15, oct = tid >> 4;
+      const int quad = th & 15, oct = th >> 4;
       const int p0 = vt_pos(quad * 4);  // 4 consecutive positions
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -154,15 +165,15 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
         const uint32_t x0 = rv[0][w], x1 = rv[1][w], x2 = rv[2][w], x3 = rv[3][w];
         u32x2_v lo{(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
         u32x2_v hi{(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-        *reinterpret_cast<u32x2_v*>(&Vs[buf][(oct * 8 + 2 * w) * LDV + p0]) = lo;
-        *reinterpret_cast<u32x2_v*>(&Vs[buf][(oct * 8 + 2 * w + 1) * LDV + p0]) = hi;
+        *reinterpret_cast<u32x2_v*>(Vs(buf) + (oct * 8 + 2 * w) * LDV + p0) = lo;
+        *reinterpret_cast<u32x2_v*>(Vs(buf) + (oct * 8 + 2 * w + 1) * LDV + p0) = hi;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
-        const int c = tid + i * 256, key = c >> 5, cc = c & 31;
-        st16(&Ks[buf][key * LDK + cc * EPC], rk[i]);
-        st16(&Vs[buf][key * LDV + cc * EPC], rv[i]);
+        const int c = th + i * 256, key = c >> 5, cc = c & 31;
+        st16(Ks(buf) + key * LDK + cc * EPC, rk[i]);
+        st16(Vs(buf) + key * LDV + cc * EPC, rv[i]);
       }
     }
   };
@@ -172,22 +183,30 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
   for (int db = 0; db < 4; ++db) o[db] = f32x16_v{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
+  // One key tile from LDS stage `buf`.
+  auto tile = [&](int kt, int buf) {
     if (wave_active && kt * BN <= w_tok_hi) {
       // S^T = K Q^T (raw scores; the 1/sqrt(d) and log2(e) scale is applied
       // inside the exponent, and max() commutes with a positive scale)
+      // The NKB accumulation chains are interleaved, and each k-step's K
+      // fragments are read from LDS one step ahead of their MFMAs.
       f32x16_v s[NKB];
+      const T* ks_ptr = Ks(buf) + c32 * LDK + hk * MF::KL;
+      typename MF::frag kf[2][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = f32x16_v{};
-        const T* ks_ptr = &Ks[buf][(kb * 32 + c32) * LDK + hk * MF::KL];
+        kf[0][kb] = MF::load(ks_ptr + kb * 32 * LDK);
+      }
 #pragma unroll
-        for (int ks = 0; ks < DSTEPS; ++ks) s[kb] = MF::run(MF::load(ks_ptr + ks * MF::K), qf[ks], s[kb]);
+      for (int ks = 0; ks < DSTEPS; ++ks) {
+        if (ks + 1 < DSTEPS) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            kf[(ks + 1) & 1][kb] = MF::load(ks_ptr + kb * 32 * LDK + (ks + 1) * MF::K);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = MF::run(kf[ks & 1][kb], qf[ks], s[kb]);
       }
       // causal mask (only tiles that cross this wave's diagonal), running max
       if (kt * BN + BN - 1 > w_tok_lo) {
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
           const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, u32x4_v{w0, w1, w2, w3});
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const T* vp = &Vs[buf][(db * 32 + c32) * LDV + ks2 * 16 + hk * 8];
+            const T* vp = Vs(buf) + (db * 32 + c32) * LDV + ks2 * 16 + hk * 8;
             o[db] = MF::run(MF::load(vp), pf, o[db]);
           }
         }
@@ -254,12 +273,64 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(const T* __restri
             const int key = kb * 32 + 8 * (st >> 2) + 4 * hk + (st & 3);
 #pragma unroll
             for (int db = 0; db < 4; ++db)
-              o[db] = MF::run(Vs[buf][key * LDV + db * 32 + c32], s[kb][st], o[db]);
+              o[db] = MF::run(Vs(buf)[key * LDV + db * 32 + c32], s[kb][st], o[db]);
           }
       }
     }
-    if (kt + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // Key halves: half 0 takes tiles [0, n0), half 1 tiles [n0, ntiles).  Each
+  // half has two LDS stages (kh*2, kh*2+1) fed from two register sets: tile
+  // i+2's global loads are issued while tile i runs, and tile i+1 (loaded one
+  // iteration earlier) is staged after it.  Both halves run n0 iterations so
+  // every wave meets every barrier.
+  const int n0 = KSPLIT == 2 ? (ntiles + 1) / 2 : ntiles;
+  const int base = kh ? n0 : 0;
+  const int cnt = kh ? ntiles - n0 : n0;
+  const int s0 = kh * 2, s1 = kh * 2 + 1;
+  if (cnt > 0) {
+    gload(base, rkA, rvA);
+    sstore(s0, rkA, rvA);
+  }
+  if (cnt > 1) gload(base + 1, rkB, rvB);
+  lds_barrier();
+  for (int i = 0; i < n0; i += 2) {
+    if (i + 2 < cnt) gload(base + i + 2, rkA, rvA);
+    if (i < cnt) tile(base + i, s0);
+    if (i + 1 < cnt) sstore(s1, rkB, rvB);
+    lds_barrier();
+    if (i + 1 >= n0) break;
+    if (i + 3 < cnt) gload(base + i + 3, rkB, rvB);
+    if (i + 1 < cnt) tile(base + i + 1, s1);
+    if (i + 2 < cnt) sstore(s0, rkA, rvA);
+    lds_barrier();
+  }
+
+  // Merge the two key halves: half 1 hands (O, m, l) to half 0 through LDS,
+  // as [block][register][lane] so every access is one contiguous row.
+  if constexpr (KSPLIT == 2) {
+  float* comb = reinterpret_cast<float*>(smem) + qblk * 66 * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) comb[(db * 16 + i) * 64 + lane] = o[db][i];
+    comb[64 * 64 + lane] = m_run;
+    comb[65 * 64 + lane] = l_run;
+  }
+  lds_barrier();
+  if (kh == 1) return;
+  {
+    const float m1 = comb[64 * 64 + lane], l1 = comb[65 * 64 + lane];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
+    const float a1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - M);
+    l_run = a0 * l_run + a1 * l1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = a0 * o[db][i] + a1 * comb[(db * 16 + i) * 64 + lane];
+  }
   }
 
   if (!row_ok) return;
@@ -289,8 +360,16 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
   const int n_rep = n_q / n_kv;
   const int tiles = (T_len * n_rep + 127) / 128;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHeadDim));
-  hipLaunchKernelGGL(flash_prefill_kernel<T>, dim3(tiles * B * n_kv), dim3(256), 0, s, Q, Kc, Vc,
-                     Out, B, T_len, n_q, n_kv, cap, scale_log2);
+  // Few query tiles: split each tile's key range over two wave groups so both
+  // waves of a SIMD serve the same tile.  Many tiles: 4-wave workgroups, two
+  // resident per CU.
+  const int wgs = tiles * B * n_kv;
+  if (wgs < 4 * 256)
+    hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
+                       T_len, n_q, n_kv, cap, scale_log2);
+  else
+    hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
+                       T_len, n_q, n_kv, cap, scale_log2);
   return hipGetLastError();
 }
 
