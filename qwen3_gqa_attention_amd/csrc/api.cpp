@@ -50,8 +50,9 @@ qwen3_attn_status check_desc(const qwen3_attn_desc* d) {
 }
 
 struct WsLayout {
-  size_t q_off, a_off, cs_off, acc_off, ml_off, total;
+  size_t q_off, a_off, cs_off, acc_off, ml_off, part_off, total;
   int nchunk;
+  bool part;  // decode projections run split-K through the part region
 };
 
 bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, int64_t cap,
@@ -66,8 +67,9 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
     L->q_off = 0;
     L->a_off = qb;
     L->cs_off = 2 * qb;
-    L->acc_off = L->ml_off = 0;
+    L->acc_off = L->ml_off = L->part_off = 0;
     L->nchunk = 0;
+    L->part = false;
     L->total = L->cs_off + align_up((size_t)n * T * 64 * 2 * sizeof(float));
     return true;
   }
@@ -82,7 +84,17 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
   L->cs_off = 2 * qb;
   L->acc_off = L->cs_off + align_up((size_t)n * 64 * 2 * sizeof(float));
   L->ml_off = L->acc_off + align_up(slots * 128 * sizeof(float));
-  L->total = L->ml_off + align_up(slots * 2 * sizeof(float));
+  L->part_off = L->ml_off + align_up(slots * 2 * sizeof(float));
+  L->part = n <= 64;
+  size_t part_floats = 0;
+  if (L->part) {
+    const int es_i = static_cast<int>(es);
+    const int nqkv = (d->n_q + 2 * d->n_kv) * 128;
+    const size_t a = q3::small_m_partial_floats(n, nqkv, d->d_model, es_i);
+    const size_t b = q3::small_m_partial_floats(n, d->d_model, d->n_q * 128, es_i);
+    part_floats = a > b ? a : b;
+  }
+  L->total = L->part_off + align_up(part_floats * sizeof(float));
   L->nchunk = (int)nchunk;
   return true;
 }
@@ -132,7 +144,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), M, nqkv, d.d_model,
-                                        e, s);
+                                        e, s, nullptr, h->inv_freq);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 1);
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
@@ -141,7 +153,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
-                              M, d.d_model, hq, s);
+                              M, d.d_model, hq, s, nullptr);
   mark_done(h, s);
   return hip_status(r);
 }
@@ -159,11 +171,15 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
                     d.n_q, d.n_kv, cap, 1, 1, d.eps};
   mark(h, s, 0);
-  hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, N, s);
-  if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  float* part = L.part ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
+  hipError_t r = hipSuccess;
+  if (!part) {  // the split-K finishing kernel evaluates RoPE itself
+    r = q3::launch_rope_table(positions, h->inv_freq, cs, N, s);
+    if (r != hipSuccess) return QWEN3_ATTN_EHIP;
+  }
   r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), N, nqkv, d.d_model,
-                                        e, s);
+                                        e, s, part, h->inv_freq);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   q3::DecodeScratch sc{reinterpret_cast<float*>(ws + L.acc_off),
                        reinterpret_cast<float*>(ws + L.ml_off), L.nchunk,
@@ -175,7 +191,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
-                              N, d.d_model, hq, s);
+                              N, d.d_model, hq, s, part);
   mark_done(h, s);
   return hip_status(r);
 }

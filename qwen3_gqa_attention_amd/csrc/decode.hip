@@ -23,7 +23,7 @@
 namespace q3 {
 
 constexpr int kDecodeChunk = 512;  // keys per workgroup
-constexpr int kDecodeUnroll = 2;   // keys per 16-lane group per iteration
+constexpr int kDecodeUnroll = 4;   // keys per 16-lane group per iteration
 
 int decode_chunk_keys() { return kDecodeChunk; }
 
@@ -114,20 +114,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d = fmaf(q[r][e], kr[u].at(e), d);
-        d = wave_xor_sum(d, 1, 8);
+        d = row16_sum(d);
         sc[u] = val[u] ? d : -INFINITY;
         mx = fmaxf(mx, sc[u]);
       }
       if (mx == -INFINITY) continue;  // uniform within the 16-lane group
       const float m_new = fmaxf(m[r], mx);
-      const float alpha = exp2f(m[r] - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m[r] - m_new);
       m[r] = m_new;
       l[r] *= alpha;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = exp2f(sc[u] - m_new);
+        const float p = __builtin_amdgcn_exp2f(sc[u] - m_new);
         l[r] += p;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, vr[u].at(e), acc[r][e]);
@@ -185,26 +185,45 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
   }
 }
 
-// Merge the key chunks of each (sequence, query head): grid (n_q, N), 128 threads.
+// Merge the key chunks of each (sequence, query head): grid (n_q, N), 128
+// threads (one per dim).  One online pass; 16 chunks' partials are loaded
+// together so their latencies overlap.
 template <typename T>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part_acc,
                                                              const float* __restrict__ part_ml,
                                                              const int32_t* __restrict__ positions,
                                                              T* __restrict__ Out, int n_q, int n_kv,
                                                              int nchunk) {
+  constexpr int U = 16;
   const int head = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int n_rep = n_q / n_kv;
   const int g = head / n_rep, r = head % n_rep;
   const int nc = (positions[s] + 1 + kDecodeChunk - 1) / kDecodeChunk;
   const size_t base = (size_t)(s * n_kv + g) * nchunk;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, part_ml[((base + c) * n_rep + r) * 2]);
-  float a = 0.f, lt = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const size_t sl = (base + c) * n_rep + r;
-    const float w = exp2f(part_ml[sl * 2] - M);
-    lt += w * part_ml[sl * 2 + 1];
-    a += w * part_acc[sl * kHeadDim + d];
+  float M = -INFINITY, a = 0.f, lt = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += U) {
+    float mv[U], lv[U], av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t sl = (base + c0 + u) * n_rep + r;
+      const bool ok = c0 + u < nc;
+      mv[u] = ok ? part_ml[sl * 2] : -INFINITY;
+      lv[u] = ok ? part_ml[sl * 2 + 1] : 0.f;
+      av[u] = ok ? part_acc[sl * kHeadDim + d] : 0.f;
+    }
+    float mx = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);
+    const float sc = exp2f(M - mx);   // 0 on the first pass (M = -inf, mx finite)
+    a *= sc;
+    lt *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = exp2f(mv[u] - mx);
+      a = fmaf(w, av[u], a);
+      lt = fmaf(w, lv[u], lt);
+    }
+    M = mx;
   }
   Out[(size_t)s * n_q * kHeadDim + head * kHeadDim + d] = from_f32<T>(a / lt);
 }

@@ -129,6 +129,16 @@ __device__ __forceinline__ float half_wave_sum(float v) {
   return v;
 }
 
+// Sum over each 16-lane DPP row (lanes 16r .. 16r+15); every lane of the row
+// gets the row's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  v += dpp_move<0x140>(v);  // row_mirror
+  return v;
+}
+
 // xor-butterfly reductions across lanes.
 __device__ __forceinline__ float wave_xor_sum(float v, int mask_lo, int mask_hi) {
   for (int m = mask_lo; m <= mask_hi; m <<= 1) v += __shfl_xor(v, m, kWave);

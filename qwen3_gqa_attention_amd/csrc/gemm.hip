@@ -98,7 +98,7 @@ __device__ __forceinline__ int swz(int row, int k) {
   return row * (8 * EPC) + ((((k / EPC) ^ (row >> 1)) & 7) * EPC) + (k % EPC);
 }
 
-template <typename T, int WM, int WN, int MI, int NI, bool QKV>
+template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restrict__ A,
                                                                 const T* __restrict__ B, int M,
                                                                 int N, int K, QkvEpilogue qe,
@@ -167,7 +167,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_v{};
 
-  const int KT = K / BK;
+  // Split-K (PARTIAL): blockIdx.y picks a K slice of K / gridDim.y; the fp32
+  // partial tile goes to se.c as [gridDim.y][M][N].
+  const int KT = K / BK / (PARTIAL ? gridDim.y : 1);
+  if constexpr (PARTIAL) {
+    const size_t koff = (size_t)blockIdx.y * KT * BK;
+    A += koff;
+    B += koff;
+  }
   const int arow = wm * 32 * MI + c32;   // this lane's first A row in the tile
   const int brow = wn * 32 * NI + c32;   // this lane's first B row in the tile
   gload(0);
@@ -197,6 +204,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 
   // ------------------------------------------------------------------ epilogue
   const int row_base = m0 + wm * 32 * MI;
+  if constexpr (PARTIAL) {
+    float* P = reinterpret_cast<float*>(se.c) + (size_t)blockIdx.y * M * N;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = row_base + mi * 32 + mfma32_row(i, lane);
+        if (row < M) {
+          float* dst = P + (size_t)row * N + n0 + wn * 32 * NI + c32;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) dst[ni * 32] = acc[mi][ni][i];
+        }
+      }
+    return;
+  }
   int head = 0, kind = 3;  // kind 3: plain projection output
   if constexpr (QKV) {
     // This wave's 128 columns are head (n0/128 + wn): [0, n_q) query heads,
@@ -292,15 +314,115 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
   }
 }
 
-template <typename T, int WM, int WN, int MI, int NI, bool QKV>
+template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false>
 static hipError_t launch_gemm(const T* A, const T* B, int M, int N, int K, const QkvEpilogue& qe,
-                              const StoreEpilogue& se, hipStream_t s) {
+                              const StoreEpilogue& se, hipStream_t s, int ksplit = 1) {
   constexpr int BM = 32 * MI * WM;
   constexpr int BN = 32 * NI * WN;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV>), dim3(tiles), dim3(WM * WN * 64), 0,
-                     s, A, B, M, N, K, qe, se);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV, PARTIAL>), dim3(tiles, ksplit),
+                     dim3(WM * WN * 64), 0, s, A, B, M, N, K, qe, se);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode-sized projections (M <= 64 rows): bound by reading the weights, so
+// the K dimension is split over the grid (many workgroups streaming weights
+// at once) into fp32 partials, which a second kernel sums.
+// ---------------------------------------------------------------------------
+constexpr int kSmallM = 64;
+
+// Number of K slices for a decode projection: about 256 workgroups, each
+// slice a whole number of 128-byte k-tiles.
+template <typename T>
+static int small_m_ksplit(int N, int K) {
+  constexpr int BK = 128 / sizeof(T);
+  const int tiles = N / 128;
+  int ks = 1;
+  while (tiles * ks * 2 <= 256 && (K / BK) % (ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+int small_m_partial_floats(int M, int N, int K, int es) {
+  const int ks = es == 2 ? small_m_ksplit<bf16_t>(N, K) : small_m_ksplit<float>(N, K);
+  return ks * M * N;
+}
+
+// Sum the K-slice partials of the q/k/v projection for one head (128
+// columns) and 16 rows, then QK-Norm, RoPE and the stores, as the GEMM
+// epilogue does.  256 threads: row = 16 * blockIdx.y + tid / 16 (one DPP row
+// of 16 lanes per token), columns 8 * (tid % 16) .. + 7.  cos/sin are
+// evaluated here from positions and omega / (2 pi) (hi + lo floats).
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
+                                                         int M, int N, QkvEpilogue qe,
+                                                         const float* __restrict__ inv_freq) {
+  const int head = blockIdx.x;
+  const int tid = threadIdx.x, j = tid & 15;
+  const int row = blockIdx.y * 16 + (tid >> 4);
+  const int kind = head < qe.n_q ? 0 : (head < qe.n_q + qe.n_kv ? 1 : 2);
+  const bool ok = row < M;
+  const int r = ok ? row : 0;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  for (int k = 0; k < ks; ++k) {
+    const float* p = part + ((size_t)k * M + r) * N + head * kHeadDim + j * 8;
+    const f32x4_v x0 = *reinterpret_cast<const f32x4_v*>(p);
+    const f32x4_v x1 = *reinterpret_cast<const f32x4_v*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] += x0[e];
+      v[4 + e] += x1[e];
+    }
+  }
+  if (kind != 2) {
+    // RMS over the head's 128 columns: 8 per thread, 16 threads per row.
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+    ss = row16_sum(ss);
+    const float rs = rsqrtf(ss * (1.f / 128.f) + qe.eps);
+    const T* g = reinterpret_cast<const T*>(kind == 0 ? qe.gq : qe.gk);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= rs * to_f32<T>(g[j * 8 + e]);
+    // RoPE: column c pairs with c + 64, i.e. thread j with j ^ 8 (DPP row_ror:8).
+    const int pos = qe.positions[r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int f = (j & 7) * 8 + e;
+      float sn, cn;
+      rope_sincos(pos, inv_freq[f], inv_freq[64 + f], &sn, &cn);
+      const float other = dpp_move<0x128>(v[e]);
+      v[e] = (j < 8) ? v[e] * cn - other * sn : v[e] * cn + other * sn;
+    }
+  }
+  if (!ok) return;
+  T* dst;
+  if (kind == 0) {
+    dst = reinterpret_cast<T*>(qe.q_out) + (size_t)row * (qe.n_q * kHeadDim) + head * kHeadDim;
+  } else {
+    const int g = head - qe.n_q - (kind == 2 ? qe.n_kv : 0);
+    const int seq = qe.decode ? row : row / qe.rows_per_seq;
+    const int slot = qe.decode ? qe.positions[row] : row % qe.rows_per_seq;
+    T* cache = reinterpret_cast<T*>(kind == 1 ? qe.k_cache : qe.v_cache);
+    dst = cache + ((size_t)(seq * qe.n_kv + g) * qe.cap + slot) * kHeadDim;
+  }
+  dst += j * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = from_f32<T>(v[e]);
+}
+
+// out[m][n] = sum over K slices of part[k][m][n], rounded to T.
+template <typename T>
+__global__ __launch_bounds__(64) void sum_partials_kernel(const float* __restrict__ part, int ks,
+                                                          int MN, T* __restrict__ out) {
+  const int i = (blockIdx.x * 64 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  f32x4_v a = *reinterpret_cast<const f32x4_v*>(part + i);
+  for (int k = 1; k < ks; ++k) a += *reinterpret_cast<const f32x4_v*>(part + (size_t)k * MN + i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[i + j] = from_f32<T>(a[j]);
 }
 
 constexpr int kCus = 256;
@@ -310,8 +432,17 @@ constexpr int kCus = 256;
 // waits).  Mid-size: 128x128 tiles.  Decode-sized M <= 64: 64x128 tiles.
 template <typename T>
 hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const QkvEpilogue& e,
-                           hipStream_t s) {
+                           hipStream_t s, float* part, const float* inv_freq) {
   StoreEpilogue se{nullptr, 0};
+  if (M <= kSmallM && part) {
+    const int ks = small_m_ksplit<T>(N, K);
+    StoreEpilogue ps{part, N};
+    hipError_t r = launch_gemm<T, 2, 1, 1, 4, false, true>(X, Wqkv, M, N, K, e, ps, s, ks);
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL(qkv_finish_kernel<T>, dim3(N / kHeadDim, (M + 15) / 16), dim3(256), 0, s,
+                       part, ks, M, N, e, inv_freq);
+    return hipGetLastError();
+  }
   if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
   if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus)
     return launch_gemm<T, 4, 2, 2, 4, true>(X, Wqkv, M, N, K, e, se, s);
@@ -319,9 +450,19 @@ hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const
 }
 
 template <typename T>
-hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, hipStream_t s) {
+hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, hipStream_t s,
+                            float* part) {
   QkvEpilogue qe{};
   StoreEpilogue se{C, N};
+  if (M <= kSmallM && part) {
+    const int ks = small_m_ksplit<T>(N, K);
+    StoreEpilogue ps{part, N};
+    hipError_t r = launch_gemm<T, 2, 1, 1, 4, false, true>(A, W, M, N, K, qe, ps, s, ks);
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL(sum_partials_kernel<T>, dim3((M * N / 4 + 63) / 64), dim3(64), 0, s, part,
+                       ks, M * N, C);
+    return hipGetLastError();
+  }
   if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, false>(A, W, M, N, K, qe, se, s);
   if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus)
     return launch_gemm<T, 4, 2, 2, 4, false>(A, W, M, N, K, qe, se, s);
@@ -329,12 +470,12 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
 }
 
 template hipError_t launch_qkv_gemm<float>(const float*, const float*, int, int, int,
-                                           const QkvEpilogue&, hipStream_t);
+                                           const QkvEpilogue&, hipStream_t, float*, const float*);
 template hipError_t launch_qkv_gemm<bf16_t>(const bf16_t*, const bf16_t*, int, int, int,
-                                            const QkvEpilogue&, hipStream_t);
+                                            const QkvEpilogue&, hipStream_t, float*, const float*);
 template hipError_t launch_proj_gemm<float>(const float*, const float*, float*, int, int, int,
-                                            hipStream_t);
+                                            hipStream_t, float*);
 template hipError_t launch_proj_gemm<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, int, int, int,
-                                             hipStream_t);
+                                             hipStream_t, float*);
 
 }  // namespace q3

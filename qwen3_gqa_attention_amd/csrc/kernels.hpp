@@ -31,13 +31,21 @@ hipError_t launch_rope_table(const int32_t* positions, const float* inv_freq, fl
                              hipStream_t s);
 
 // q/k/v projection X[M,K] * Wqkv[N,K]^T with the fused epilogue; N = (n_q + 2 n_kv) * 128.
+// `part` (may be null): fp32 scratch of small_m_partial_floats(M, N, K) floats;
+// with it, M <= 64 runs as a split-K GEMM plus a finishing kernel, which
+// evaluates RoPE from `inv_freq` itself (e.rope_cs is not read then).
 template <typename T>
 hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K,
-                           const QkvEpilogue& e, hipStream_t s);
+                           const QkvEpilogue& e, hipStream_t s, float* part,
+                           const float* inv_freq);
 
-// Plain projection C[M,N] = A[M,K] * W[N,K]^T (o_proj).
+// Plain projection C[M,N] = A[M,K] * W[N,K]^T (o_proj); `part` as above.
 template <typename T>
-hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, hipStream_t s);
+hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, hipStream_t s,
+                            float* part);
+
+// fp32 scratch (floats) the split-K path of an M <= 64 projection needs.
+int small_m_partial_floats(int M, int N, int K, int elem_size);
 
 // Causal GQA flash attention over the freshly written caches.
 template <typename T>

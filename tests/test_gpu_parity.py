@@ -242,7 +242,9 @@ def test_decode_equals_last_prefill_row_on_gpu():
     yd = blk.decode(x[:, T - 1].contiguous(), torch.full((2,), T - 1, dtype=torch.int32, device="cuda"), kc2, vc2)
     torch.cuda.synchronize()
     assert_close(host(yd), host(y[:, T - 1]), w.dtype, "decode vs last prefill row")
-    np.testing.assert_array_equal(host(kc2[:, :, T - 1]), host(kc[:, :, T - 1]))
+    # the same key computed by the decode and the prefill projections
+    # (different accumulation orders, so equal up to bf16 rounding)
+    assert_close(host(kc2[:, :, T - 1]), host(kc[:, :, T - 1]), w.dtype, "new k: decode vs prefill")
     blk.close()
 
 
