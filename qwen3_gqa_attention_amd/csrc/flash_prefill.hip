@@ -40,9 +40,15 @@ template <typename T> struct FlashTile;
 template <> struct FlashTile<bf16_t> { static constexpr int BN = 64; };
 template <> struct FlashTile<float> { static constexpr int BN = 32; };
 
-// Position, inside its 16-key group, of key k in the transposed V tile.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+typedef __bf16 v4bf16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4bf16_t lds_v4bf16_t;
+
+// Transposing LDS read (ds_read_b64_tr_b16): inside each 16-lane group, lane
+// i receives element i % 4 of the 8-byte rows addressed by lanes i / 4,
+// i / 4 + 4, i / 4 + 8 and i / 4 + 12.
+__device__ __forceinline__ v4bf16_t ds_read_tr16(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_v4bf16_t*)(__attribute__((address_space(3))) bf16_t*)(p));
 }
 
 template <typename T, int KSPLIT>
@@ -56,10 +62,13 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   constexpr int BN = FlashTile<T>::BN;
   constexpr int NKB = BN / 32;                 // 32-key blocks per tile
   constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
-  constexpr int LDK = kHeadDim + EPC;          // K tile row (elements)
-  constexpr bool VT = sizeof(T) == 2;          // V staged transposed (bf16)
-  constexpr int LDV = VT ? (BN + 8) : LDK;
-  constexpr int VSZ = VT ? kHeadDim * LDV : BN * LDV;
+  constexpr bool VT = sizeof(T) == 2;          // bf16: DMA staging + transposing V reads
+  // bf16 tiles are unpadded 256-byte rows filled by direct global->LDS loads
+  // (16-byte chunks XOR-swizzled per row); fp32 tiles are padded rows
+  // written from registers.
+  constexpr int LDK = VT ? kHeadDim : kHeadDim + EPC;  // K tile row (elements)
+  constexpr int LDV = LDK;
+  constexpr int VSZ = BN * LDV;
   constexpr int KCH = BN * (kHeadDim / EPC) / 256;  // K chunks per thread per tile
   constexpr int DSTEPS = kHeadDim / MF::K;     // MFMA steps over d_head
 
@@ -112,69 +121,50 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const T* Kg = Kc + (size_t)(b * n_kv + g) * cap * kHeadDim;
   const T* Vg = Vc + (size_t)(b * n_kv + g) * cap * kHeadDim;
 
-  u32x4_v rkA[KCH], rvA[KCH], rkB[KCH], rvB[KCH];
-  // Per-thread K/V row pointers for tile 0; each tile advances them by BN rows.
-  // bf16: K rows (tid >> 4) + 16 i, chunk tid & 15; V keys 4 (tid & 15) + d,
-  // dims 8 (tid >> 4) .. + 7 (the thread owns 4 consecutive keys x 8 dims).
-  const int k_row0 = VT ? (th >> 4) : 0;
-  const int v_key0 = VT ? (th & 15) * 4 : 0;
-  const T* kp = Kg + (size_t)k_row0 * kHeadDim + (VT ? (th & 15) * EPC : 0);
-  const T* vp0 = Vg + (size_t)v_key0 * kHeadDim + (VT ? (th >> 4) * 8 : 0);
-  auto gload = [&](int kt, u32x4_v (&rk)[KCH], u32x4_v (&rv)[KCH]) {
+  // ---- bf16 staging: direct global -> LDS loads -------------------------
+  // One wave instruction (global_load_lds_dwordx4) fills 1 KB = 4 rows of
+  // 256 bytes; lane i lands on row i / 16, physical chunk i % 16.  K rows use
+  // physical chunk = logical ^ (row & 15): the 16 rows that one K-fragment
+  // read touches per bank pass hit 16 different chunks.  V rows use
+  // logical ^ 4 * (row & 3): a transposing V read covers 4 rows x 4 chunks.
+  // Key rows past the sequence load its last row instead (always written, so
+  // finite); the causal mask zeroes their weight.
+  const int hw = wave & 3;  // wave index inside its key half
+  auto dma_tile = [&](int kt, int buf) {
     const int kbase = kt * BN;
-    if constexpr (VT) {
-      const T* kpt = kp + (size_t)kbase * kHeadDim;
-      const T* vpt = vp0 + (size_t)kbase * kHeadDim;
-      if (kbase + BN <= T_len) {
+    const int rsub = lane >> 4, p = lane & 15;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) rk[i] = ld16(kpt + (size_t)i * 16 * kHeadDim);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) rv[d] = ld16(vpt + (size_t)d * kHeadDim);
-      } else {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i)
-          rk[i] = (kbase + k_row0 + 16 * i < T_len) ? ld16(kpt + (size_t)i * 16 * kHeadDim)
-                                                    : u32x4_v{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          rv[d] = (kbase + v_key0 + d < T_len) ? ld16(vpt + (size_t)d * kHeadDim) : u32x4_v{0u, 0u, 0u, 0u};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int c = th + i * 256, key = c >> 5, cc = c & 31;
-        const size_t off = (size_t)(kbase + key) * kHeadDim + cc * EPC;
-        const bool ok = kbase + key < T_len;
-        rk[i] = ok ? ld16(Kg + off) : u32x4_v{0u, 0u, 0u, 0u};
-        rv[i] = ok ? ld16(Vg + off) : u32x4_v{0u, 0u, 0u, 0u};
-      }
+    for (int j = 0; j < BN / 16; ++j) {
+      const int r = (j * 4 + hw) * 4 + rsub;       // row in the tile
+      const int key = min(kbase + r, T_len - 1);
+      const int r4 = (j * 4 + hw) * 4;              // first row of this instruction
+      const T* gk = Kg + (size_t)key * kHeadDim + ((p ^ (r & 15)) * EPC);
+      const T* gv = Vg + (size_t)key * kHeadDim + ((p ^ (4 * (r & 3))) * EPC);
+      dma16_to_lds(gk, Ks(buf) + r4 * LDK);
+      dma16_to_lds(gv, Vs(buf) + r4 * LDV);
     }
   };
-  auto sstore = [&](int buf, const u32x4_v (&rk)[KCH], const u32x4_v (&rv)[KCH]) {
-    if constexpr (VT) {
+
+  // ---- fp32 staging: registers -> LDS ----------------------------------
+  constexpr int RCH = VT ? 1 : KCH;
+  u32x4_v rkA[RCH], rvA[RCH];
+  auto gload = [&](int kt) {
+    const int kbase = kt * BN;
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int c = th + i * 256, key = c >> 4, cc = c & 15;
-        st16(Ks(buf) + key * LDK + cc * EPC, rk[i]);
-      }
-      const int quad = th & 15, oct = th >> 4;
-      const int p0 = vt_pos(quad * 4);  // 4 consecutive positions
+    for (int i = 0; i < RCH; ++i) {
+      const int c = th + i * 256, key = c >> 5, cc = c & 31;
+      const size_t off = (size_t)(kbase + key) * kHeadDim + cc * EPC;
+      const bool ok = kbase + key < T_len;
+      rkA[i] = ok ? ld16(Kg + off) : u32x4_v{0u, 0u, 0u, 0u};
+      rvA[i] = ok ? ld16(Vg + off) : u32x4_v{0u, 0u, 0u, 0u};
+    }
+  };
+  auto sstore = [&](int buf) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims oct*8 + 2w (low halves) and oct*8 + 2w + 1 (high halves)
-        const uint32_t x0 = rv[0][w], x1 = rv[1][w], x2 = rv[2][w], x3 = rv[3][w];
-        u32x2_v lo{(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-        u32x2_v hi{(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-        *reinterpret_cast<u32x2_v*>(Vs(buf) + (oct * 8 + 2 * w) * LDV + p0) = lo;
-        *reinterpret_cast<u32x2_v*>(Vs(buf) + (oct * 8 + 2 * w + 1) * LDV + p0) = hi;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int c = th + i * 256, key = c >> 5, cc = c & 31;
-        st16(Ks(buf) + key * LDK + cc * EPC, rk[i]);
-        st16(Vs(buf) + key * LDV + cc * EPC, rv[i]);
-      }
+    for (int i = 0; i < RCH; ++i) {
+      const int c = th + i * 256, key = c >> 5, cc = c & 31;
+      st16(Ks(buf) + key * LDK + cc * EPC, rkA[i]);
+      st16(Vs(buf) + key * LDV + cc * EPC, rvA[i]);
     }
   };
 
@@ -191,19 +181,24 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
       // The NKB accumulation chains are interleaved, and each k-step's K
       // fragments are read from LDS one step ahead of their MFMAs.
       f32x16_v s[NKB];
-      const T* ks_ptr = Ks(buf) + c32 * LDK + hk * MF::KL;
+      const T* ks_ptr = Ks(buf) + c32 * LDK;
+      // element offset of this lane's K fragment for MFMA step ks
+      auto koff = [&](int ks) {
+        if constexpr (VT) return (((2 * ks + hk) ^ (c32 & 15)) * EPC);  // row & 15 == c32 & 15
+        else return ks * MF::K + hk * MF::KL;
+      };
       typename MF::frag kf[2][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = f32x16_v{};
-        kf[0][kb] = MF::load(ks_ptr + kb * 32 * LDK);
+        kf[0][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(0));
       }
 #pragma unroll
       for (int ks = 0; ks < DSTEPS; ++ks) {
         if (ks + 1 < DSTEPS) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            kf[(ks + 1) & 1][kb] = MF::load(ks_ptr + kb * 32 * LDK + (ks + 1) * MF::K);
+            kf[(ks + 1) & 1][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(ks + 1));
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s[kb] = MF::run(kf[ks & 1][kb], qf[ks], s[kb]);
@@ -254,8 +249,20 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
           const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, u32x4_v{w0, w1, w2, w3});
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const T* vp = Vs(buf) + (db * 32 + c32) * LDV + ks2 * 16 + hk * 8;
-            o[db] = MF::run(MF::load(vp), pf, o[db]);
+            // V^T fragment (dim db*32 + c32; the 8 keys whose P this lane
+            // packed: ks2*16 + 4*hk + {0..3} and + 8 + {0..3}) from two
+            // transposing reads of the row-major V tile.  In each read,
+            // lane j of a 16-lane group addresses key K0 + j/4, dims
+            // D0 + 4*(j%4) .. +3, and receives dim D0 + j of keys K0 .. K0+3.
+            const int j = lane & 15;
+            const int key0 = ks2 * 16 + 4 * hk + (j >> 2);
+            const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+            const int ch = (d >> 3) ^ (4 * (key0 & 3));  // key0 + 8 has the same key & 3
+            const int eo = ch * EPC + (d & 7);
+            const v4bf16_t lo = ds_read_tr16(Vs(buf) + key0 * LDV + eo);
+            const v4bf16_t hi = ds_read_tr16(Vs(buf) + (key0 + 8) * LDV + eo);
+            const bf16x8_v vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[db] = MF::run(vf, pf, o[db]);
           }
         }
         l_run += lsum;
@@ -288,22 +295,30 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int base = kh ? n0 : 0;
   const int cnt = kh ? ntiles - n0 : n0;
   const int s0 = kh * 2, s1 = kh * 2 + 1;
-  if (cnt > 0) {
-    gload(base, rkA, rvA);
-    sstore(s0, rkA, rvA);
-  }
-  if (cnt > 1) gload(base + 1, rkB, rvB);
-  lds_barrier();
-  for (int i = 0; i < n0; i += 2) {
-    if (i + 2 < cnt) gload(base + i + 2, rkA, rvA);
-    if (i < cnt) tile(base + i, s0);
-    if (i + 1 < cnt) sstore(s1, rkB, rvB);
+  if constexpr (VT) {
+    // Two LDS stages per key half: tile i+1's loads are issued before tile i
+    // runs into the stage that tile i-1 used (free once every wave passed the
+    // barrier that ended tile i-1).  Both halves run n0 iterations so every
+    // wave meets every barrier.
+    if (cnt > 0) dma_tile(base, s0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and tile 0
     lds_barrier();
-    if (i + 1 >= n0) break;
-    if (i + 3 < cnt) gload(base + i + 3, rkB, rvB);
-    if (i + 1 < cnt) tile(base + i + 1, s1);
-    if (i + 2 < cnt) sstore(s0, rkA, rvA);
-    lds_barrier();
+    for (int i = 0; i < n0; ++i) {
+      if (i + 1 < cnt) dma_tile(base + i + 1, (i & 1) ? s0 : s1);
+      if (i < cnt) tile(base + i, (i & 1) ? s1 : s0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i+1 has landed
+      lds_barrier();
+    }
+  } else {
+    for (int i = 0; i < n0; ++i) {
+      if (i < cnt) {
+        gload(base + i);
+        sstore(s0);
+      }
+      lds_barrier();
+      if (i < cnt) tile(base + i, s0);
+      lds_barrier();
+    }
   }
 
   // Merge the two key halves: half 1 hands (O, m, l) to half 0 through LDS,

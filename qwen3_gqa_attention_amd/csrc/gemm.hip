@@ -98,7 +98,8 @@ __device__ __forceinline__ int swz(int row, int k) {
   return row * (8 * EPC) + ((((k / EPC) ^ (row >> 1)) & 7) * EPC) + (k % EPC);
 }
 
-template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false>
+template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false,
+          int NSTAGE = 2>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restrict__ A,
                                                                 const T* __restrict__ B, int M,
                                                                 int N, int K, QkvEpilogue qe,
@@ -109,13 +110,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
   constexpr int BN = 32 * NI * WN;
   constexpr int EPC = 16 / sizeof(T);    // elements per 16-byte chunk
   constexpr int BK = 8 * EPC;            // 128 bytes of K per row
-  constexpr int A_CH = BM * 8 / NT;      // 16-byte chunks per thread per k-tile
-  constexpr int B_CH = BN * 8 / NT;
   constexpr int KS = BK / MF::K;         // MFMA k-steps per k-tile
   constexpr int STAGE = (BM + BN) * BK;  // elements per LDS stage
   // epilogue staging (bf16 only; fp32 results are stored from registers)
   constexpr int STAGED = sizeof(T) == 2 ? (NT / 64) * (32 * MI) * (32 * NI + 8) : 0;
-  constexpr int SMEM = 2 * STAGE > STAGED ? 2 * STAGE : STAGED;
+  constexpr int SMEM = NSTAGE * STAGE > STAGED ? NSTAGE * STAGE : STAGED;
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 LDS stages");
   static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads mismatch");
   static_assert(!QKV || NI == 4, "q/k/v epilogue needs one whole head per wave");
 
@@ -132,32 +132,50 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
-  u32x4_v ra[A_CH], rb[B_CH];
-  auto gload = [&](int k0) {
+  // Direct global -> LDS loads (global_load_lds_dwordx4): lane i of a wave
+  // instruction writes the 16 bytes it fetched to LDS at base + 16 * i, so one
+  // instruction fills 8 consecutive 128-byte rows.  The swizzle is applied on
+  // the global side: the lane that lands on physical chunk p of row r fetches
+  // logical chunk p ^ ((r >> 1) & 7).  No registers hold the data and no LDS
+  // store instructions are issued; the copy runs while the MFMAs do.
+  constexpr int NW = NT / 64;
+  constexpr int A_INS = BM / 8 / NW;  // wave instructions per k-tile for A
+  constexpr int B_INS = BN / 8 / NW;
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows vs waves");
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  typedef __attribute__((address_space(1))) void glb_void_t;
+  auto gload_lds = [&](int buf, int k0) {
+    char* as = reinterpret_cast<char*>(smem + buf * STAGE);
+    char* bs = as + BM * BK * sizeof(T);
+    const int rsub = lane >> 3, p = lane & 7;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * NT, r = c >> 3, cc = c & 7;
+    for (int j = 0; j < A_INS; ++j) {
+      const int rb8 = (j * NW + wave) * 8;
+      const int r = rb8 + rsub;
       const int row = min(m0 + r, M - 1);  // rows past M load a valid row; never stored
-      ra[i] = ld16(A + (size_t)row * K + k0 + cc * EPC);
+      const T* g = A + (size_t)row * K + k0 + (p ^ ((r >> 1) & 7)) * EPC;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(as + rb8 * 128), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NT, r = c >> 3, cc = c & 7;
-      rb[i] = ld16(B + (size_t)(n0 + r) * K + k0 + cc * EPC);
+    for (int j = 0; j < B_INS; ++j) {
+      const int rb8 = (j * NW + wave) * 8;
+      const int r = rb8 + rsub;
+      const T* g = B + (size_t)(n0 + r) * K + k0 + (p ^ ((r >> 1) & 7)) * EPC;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(bs + rb8 * 128), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-    T* as = smem + buf * STAGE;
-    T* bs = as + BM * BK;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * NT, r = c >> 3, cc = c & 7;
-      st16(as + swz<EPC>(r, cc * EPC), ra[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NT, r = c >> 3, cc = c & 7;
-      st16(bs + swz<EPC>(r, cc * EPC), rb[i]);
+  // Wait until at most `ahead` k-tiles of this wave's LDS-bound loads are
+  // still in flight (loads complete in issue order; s_waitcnt vmcnt(n) with
+  // the other counters left alone).
+  constexpr int INS = A_INS + B_INS;
+  static_assert(2 * INS < 64, "vmcnt range");
+  auto wait_tiles = [](int ahead) {
+    if (NSTAGE >= 4 && ahead >= 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * INS) & 15) | (((2 * INS) >> 4) << 14));
+    } else if (NSTAGE >= 3 && ahead >= 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (INS & 15) | ((INS >> 4) << 14));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     }
   };
 
@@ -177,30 +195,57 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
   }
   const int arow = wm * 32 * MI + c32;   // this lane's first A row in the tile
   const int brow = wn * 32 * NI + c32;   // this lane's first B row in the tile
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // NSTAGE LDS buffers; k-tile kt lives in buffer kt % NSTAGE and its loads
+  // are issued NSTAGE - 1 tiles ahead.
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < KT) gload_lds(st, st * BK);
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const int buf = kt % NSTAGE;
+    wait_tiles(min(NSTAGE - 2, KT - 1 - kt));  // tile kt has landed (this wave's part)
+    lds_barrier();                             // ... and every wave's; tile kt-1 is consumed
+    // The buffer refilled here held tile kt-1, which every wave finished
+    // reading before the barrier above.
+    if (kt + NSTAGE - 1 < KT) gload_lds((kt + NSTAGE - 1) % NSTAGE, (kt + NSTAGE - 1) * BK);
     const T* as = smem + buf * STAGE;
     const T* bs = as + BM * BK;
+    // Fragments are double-buffered in registers: the LDS reads of k-step
+    // ks+1 are in flight while the MI*NI MFMAs of step ks run.
+    typename MF::frag af[2][MI], bfr[2][NI];
+    auto lfrag = [&](int set, int ks) {
+      const int k = ks * MF::K + hk * MF::KL;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) af[set][mi] = MF::load(as + swz<EPC>(arow + mi * 32, k));
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) bfr[set][ni] = MF::load(bs + swz<EPC>(brow + ni * 32, k));
+    };
+    lfrag(0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);  // step 0's LDS reads first
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int k = ks * MF::K + hk * MF::KL;
-      typename MF::frag af[MI], bfr[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[mi] = MF::load(as + swz<EPC>(arow + mi * 32, k));
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bfr[ni] = MF::load(bs + swz<EPC>(brow + ni * 32, k));
+      if (ks + 1 < KS) lfrag((ks + 1) & 1, ks + 1);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = MF::run(af[mi], bfr[ni], acc[mi][ni]);
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = MF::run(af[ks & 1][mi], bfr[ks & 1][ni], acc[mi][ni]);
+      // Pin the order the scheduler would otherwise undo: each MFMA of this
+      // step is followed by one LDS read of the next step.
+      constexpr int NR = MI + NI, NM = MI * NI;
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        }
+        if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+        if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      }
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
   }
+  lds_barrier();  // the epilogue reuses the LDS of the last tiles
 
   // ------------------------------------------------------------------ epilogue
   const int row_base = m0 + wm * 32 * MI;
@@ -314,13 +359,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
   }
 }
 
-template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false>
+template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false,
+          int NSTAGE = 2>
 static hipError_t launch_gemm(const T* A, const T* B, int M, int N, int K, const QkvEpilogue& qe,
                               const StoreEpilogue& se, hipStream_t s, int ksplit = 1) {
   constexpr int BM = 32 * MI * WM;
   constexpr int BN = 32 * NI * WN;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV, PARTIAL>), dim3(tiles, ksplit),
+  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV, PARTIAL, NSTAGE>), dim3(tiles, ksplit),
                      dim3(WM * WN * 64), 0, s, A, B, M, N, K, qe, se);
   return hipGetLastError();
 }
