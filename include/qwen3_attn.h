@@ -108,7 +108,9 @@ size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
  *             >= T are not touched.  Requires T <= cache_cap.
  *   out       [B, T, d_model]
  * Workspace layout after the call (informative, for tests): the rotated
- * queries [B*T, n_q*d_head] then the merged attention output
+ * queries [B*T, n_q*d_head], stored multiplied by log2(e)/sqrt(d_head)
+ * (the factor the attention kernels need in front of their exp2), then the
+ * merged attention output
  * [B*T, n_q*d_head], both of the dtype, each padded to 256 bytes, then the
  * RoPE (cos, sin) table [B*T, d_head/2] in fp32. */
 qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,

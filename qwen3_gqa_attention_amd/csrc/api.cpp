@@ -138,7 +138,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
-                    d.n_q, d.n_kv, cap, T_len, 0, d.eps};
+                    d.n_q, d.n_kv, cap, T_len, 0, d.eps, q3::kScoreScaleLog2};
   mark(h, s, 0);
   hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, M, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
@@ -169,7 +169,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
-                    d.n_q, d.n_kv, cap, 1, 1, d.eps};
+                    d.n_q, d.n_kv, cap, 1, 1, d.eps, q3::kScoreScaleLog2};
   mark(h, s, 0);
   float* part = L.part ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
   hipError_t r = hipSuccess;

@@ -66,8 +66,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
                                                           const int32_t* __restrict__ positions,
                                                           float* __restrict__ part_acc,
                                                           float* __restrict__ part_ml, int n_q,
-                                                          int n_kv, int64_t cap, int nchunk,
-                                                          float scale_log2) {
+                                                          int n_kv, int64_t cap, int nchunk) {
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int nkeys = positions[s] + 1;
   const int k0 = c * kDecodeChunk;
@@ -88,7 +87,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
       RowSlice<T> x;
       x.load(qp + r * kHeadDim);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[r][e] = x.at(e) * scale_log2;
+      for (int e = 0; e < 8; ++e) q[r][e] = x.at(e);  // already times log2(e)/sqrt(d)
     }
   }
   float m[NREP], l[NREP], acc[NREP][8];
@@ -245,10 +244,8 @@ template <typename T, int NREP>
 static void launch_decode_nrep(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
                                int N, int n_q, int n_kv, int64_t cap, const DecodeScratch& ws,
                                hipStream_t s) {
-  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHeadDim));
   hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(ws.nchunk, n_kv, N), dim3(256), 0, s, Q,
-                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, cap, ws.nchunk,
-                     scale_log2);
+                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, cap, ws.nchunk);
 }
 
 template <typename T>

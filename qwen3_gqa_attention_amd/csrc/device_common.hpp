@@ -18,6 +18,7 @@ typedef float f32x4_v __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kHeadDim = 128;
 
+
 // ---------------------------------------------------------------------------
 // Conversions.  bf16 -> f32 is exact (a shift); f32 -> bf16 rounds to nearest
 // even (gfx950 v_cvt_pk_bf16_f32).
@@ -105,17 +106,21 @@ __device__ __forceinline__ u32x4_v ld16(const void* p) { return *reinterpret_cas
 __device__ __forceinline__ void st16(void* p, u32x4_v v) { *reinterpret_cast<u32x4_v*>(p) = v; }
 
 // 16-byte direct global -> LDS load (global_load_lds_dwordx4): lane i of the
-// wave writes the 16 bytes at `g` to LDS address lds_base + 16 * i
+// wave writes the 16 bytes at `g` to LDS byte address lds_base + 16 * i
 // (lds_base must be wave-uniform).  Written as inline asm so that the
 // compiler does not treat it as a pending write to all of LDS: it would
 // otherwise make every later LDS read it cannot disambiguate (the
 // transposing reads, for instance) wait for the load.  The instruction has
 // no result register; completion is tracked by vmcnt, so the caller waits
 // with s_waitcnt vmcnt before a barrier that publishes the data.
-__device__ __forceinline__ void dma16_to_lds(const void* g, const void* lds_base) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds_base))));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(l) : "memory", "m0");
+__device__ __forceinline__ void dma16_to_lds(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               : : "v"(g), "s"(lds_base) : "memory", "m0");
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for

@@ -56,8 +56,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc,
                                                             T* __restrict__ Out, int B, int T_len,
-                                                            int n_q, int n_kv, int64_t cap,
-                                                            float scale_log2) {
+                                                            int n_q, int n_kv, int64_t cap) {
   using MF = Mfma32<T>;
   constexpr int BN = FlashTile<T>::BN;
   constexpr int NKB = BN / 32;                 // 32-key blocks per tile
@@ -93,7 +92,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
 
   // Wave w owns query block w & 3 (32 rows) over key half w >> 2 (with
   // KSPLIT = 2; with KSPLIT = 1 four waves cover the whole key range).
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qblk = wave & 3, kh = KSPLIT == 2 ? (wave >> 2) : 0;
   const int th = tid & 255;                    // thread index inside the key half
   const int c32 = lane & 31, hk = lane >> 5;
@@ -130,18 +130,29 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // Key rows past the sequence load its last row instead (always written, so
   // finite); the causal mask zeroes their weight.
   const int hw = wave & 3;  // wave index inside its key half
+  constexpr int NDMA = VT ? BN / 16 : 1;  // DMA instructions per wave per tile (K and V each)
+  int dma_row[NDMA], dk_ch[NDMA], dv_ch[NDMA];  // lane's tile row and swizzled chunk offsets
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) {
+    const int r = (j * 4 + hw) * 4 + (lane >> 4);
+    dma_row[j] = r;
+    dk_ch[j] = ((lane & 15) ^ (r & 15)) * EPC;
+    dv_ch[j] = ((lane & 15) ^ (4 * (r & 3))) * EPC;
+  }
+  const uint32_t smem_lds = lds_addr(smem);
   auto dma_tile = [&](int kt, int buf) {
     const int kbase = kt * BN;
-    const int rsub = lane >> 4, p = lane & 15;
+    const uint32_t lk = smem_lds + (uint32_t)((Ks(buf) - smem) * sizeof(T));
+    const uint32_t lv = smem_lds + (uint32_t)((Vs(buf) - smem) * sizeof(T));
+    const bool full = kbase + BN <= T_len;  // uniform
 #pragma unroll
-    for (int j = 0; j < BN / 16; ++j) {
-      const int r = (j * 4 + hw) * 4 + rsub;       // row in the tile
-      const int key = min(kbase + r, T_len - 1);
-      const int r4 = (j * 4 + hw) * 4;              // first row of this instruction
-      const T* gk = Kg + (size_t)key * kHeadDim + ((p ^ (r & 15)) * EPC);
-      const T* gv = Vg + (size_t)key * kHeadDim + ((p ^ (4 * (r & 3))) * EPC);
-      dma16_to_lds(gk, Ks(buf) + r4 * LDK);
-      dma16_to_lds(gv, Vs(buf) + r4 * LDV);
+    for (int j = 0; j < NDMA; ++j) {
+      const int key = full ? kbase + dma_row[j] : min(kbase + dma_row[j], T_len - 1);
+      const T* krow = Kg + (size_t)key * kHeadDim;
+      const T* vrow = Vg + (size_t)key * kHeadDim;
+      const uint32_t r4b = (uint32_t)((j * 4 + hw) * 4 * LDK * sizeof(T));  // this instruction's first row
+      dma16_to_lds(krow + dk_ch[j], lk + r4b);
+      dma16_to_lds(vrow + dv_ch[j], lv + r4b);
     }
   };
 
@@ -171,28 +182,50 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   f32x16_v o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_v{};
+  // m_run: running max of the (log2-scaled) scores, -inf until this lane has
+  // seen a key.  The score accumulators start at -m_run (0 while m_run is
+  // -inf), so they come out of the MFMAs already relative to the running max.
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16_v mbias = f32x16_v{};
 
   // One key tile from LDS stage `buf`.
+  // Per-lane LDS element offsets of the fragment reads, fixed for the whole
+  // key loop (the swizzles depend on the lane only): k_off[ks] for the K
+  // fragment of MFMA step ks, v_off[db] for the first transposing V read of
+  // dim block db (other key groups add whole rows).
+  constexpr int NKOFF = VT ? DSTEPS : 1;
+  int k_off[NKOFF], v_off[4];
+#pragma unroll
+  for (int ks = 0; ks < NKOFF; ++ks)
+    k_off[ks] = c32 * LDK + (VT ? ((2 * ks + hk) ^ (c32 & 15)) * EPC : 0);
+  {
+    const int j = lane & 15;
+    const int key0 = 4 * hk + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      const int ch = (d >> 3) ^ (4 * (key0 & 3));  // same for key0 + 16 i and key0 + 8
+      v_off[db] = key0 * LDV + ch * EPC + (d & 7);
+    }
+  }
+
   auto tile = [&](int kt, int buf) {
     if (wave_active && kt * BN <= w_tok_hi) {
-      // S^T = K Q^T (raw scores; the 1/sqrt(d) and log2(e) scale is applied
-      // inside the exponent, and max() commutes with a positive scale)
+      // S^T = K Q^T - m_run.  Q carries the log2(e)/sqrt(d) factor, so the
+      // scores are already in the base-2 units of the exponent.
       // The NKB accumulation chains are interleaved, and each k-step's K
       // fragments are read from LDS one step ahead of their MFMAs.
       f32x16_v s[NKB];
-      const T* ks_ptr = Ks(buf) + c32 * LDK;
+      const T* ks_ptr = Ks(buf);
+      // The first MFMA step of each chain adds to mbias instead of zero.
       // element offset of this lane's K fragment for MFMA step ks
       auto koff = [&](int ks) {
-        if constexpr (VT) return (((2 * ks + hk) ^ (c32 & 15)) * EPC);  // row & 15 == c32 & 15
-        else return ks * MF::K + hk * MF::KL;
+        if constexpr (VT) return k_off[ks];
+        else return c32 * LDK + ks * MF::K + hk * MF::KL;
       };
       typename MF::frag kf[2][NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16_v{};
-        kf[0][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(0));
-      }
+      for (int kb = 0; kb < NKB; ++kb) kf[0][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(0));
 #pragma unroll
       for (int ks = 0; ks < DSTEPS; ++ks) {
         if (ks + 1 < DSTEPS) {
@@ -201,7 +234,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
             kf[(ks + 1) & 1][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(ks + 1));
         }
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[kb] = MF::run(kf[ks & 1][kb], qf[ks], s[kb]);
+        for (int kb = 0; kb < NKB; ++kb)
+          s[kb] = MF::run(kf[ks & 1][kb], qf[ks], ks == 0 ? mbias : s[kb]);
       }
       // causal mask (only tiles that cross this wave's diagonal), running max
       if (kt * BN + BN - 1 > w_tok_lo) {
@@ -211,25 +245,42 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
           for (int i = 0; i < 16; ++i)
             if (kt * BN + kb * 32 + mfma32_row(i, lane) > tok) s[kb][i] = -INFINITY;
       }
+      // Tile max relative to the running max; the two half-waves hold the
+      // two halves of each query's keys.
       float mloc = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[kb][i]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * scale_log2;
-      // Rescale the running sum and O only if some lane's max rose.
-      if (__ballot(mloc > m_run) != 0) {
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc),
+                                                         __float_as_uint(mloc), false, false);
+        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // A lane's max moves if this tile exceeds it, or if it is the lane's
+      // first tile with an unmasked key.  Only then are O and the sum
+      // rescaled and the scores shifted (rare after the first tiles).
+      const bool first = m_run == -INFINITY;
+      const bool moved = first ? (mloc > -INFINITY) : (mloc > 0.f);
+      if (__ballot(moved) != 0) {
+        const float delta = moved ? mloc : 0.f;
+        if (!first) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+          for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        }
+        m_run = moved ? (first ? mloc : m_run + delta) : m_run;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] -= delta;
+        const float nb = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mbias[i] = nb;
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], scale_log2, -m_run));
+        for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i]);
 
       // O^T += V^T P^T.  The running sum adds the bf16-rounded P that the
       // MFMA consumes, two at a time (dot2 with ones).
@@ -254,13 +305,9 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
             // transposing reads of the row-major V tile.  In each read,
             // lane j of a 16-lane group addresses key K0 + j/4, dims
             // D0 + 4*(j%4) .. +3, and receives dim D0 + j of keys K0 .. K0+3.
-            const int j = lane & 15;
-            const int key0 = ks2 * 16 + 4 * hk + (j >> 2);
-            const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-            const int ch = (d >> 3) ^ (4 * (key0 & 3));  // key0 + 8 has the same key & 3
-            const int eo = ch * EPC + (d & 7);
-            const v4bf16_t lo = ds_read_tr16(Vs(buf) + key0 * LDV + eo);
-            const v4bf16_t hi = ds_read_tr16(Vs(buf) + (key0 + 8) * LDV + eo);
+            const T* vq = Vs(buf) + v_off[db] + ks2 * 16 * LDV;
+            const v4bf16_t lo = ds_read_tr16(vq);
+            const v4bf16_t hi = ds_read_tr16(vq + 8 * LDV);
             const bf16x8_v vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             o[db] = MF::run(vf, pf, o[db]);
           }
@@ -374,17 +421,16 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
                                 int n_q, int n_kv, int64_t cap, hipStream_t s) {
   const int n_rep = n_q / n_kv;
   const int tiles = (T_len * n_rep + 127) / 128;
-  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHeadDim));
   // Few query tiles: split each tile's key range over two wave groups so both
   // waves of a SIMD serve the same tile.  Many tiles: 4-wave workgroups, two
   // resident per CU.
   const int wgs = tiles * B * n_kv;
   if (wgs < 4 * 256)
     hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, cap, scale_log2);
+                       T_len, n_q, n_kv, cap);
   else
     hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, cap, scale_log2);
+                       T_len, n_q, n_kv, cap);
   return hipGetLastError();
 }
 

@@ -274,7 +274,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
       float gain[4];
       const T* g = reinterpret_cast<const T*>(kind == 0 ? qe.gq : qe.gk);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) gain[ni] = to_f32<T>(g[ni * 32 + c32]);
+      for (int ni = 0; ni < 4; ++ni)
+        gain[ni] = to_f32<T>(g[ni * 32 + c32]) * (kind == 0 ? qe.q_scale : 1.f);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         float2 cs0[16], cs1[16];
@@ -430,8 +431,9 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
     ss = row16_sum(ss);
     const float rs = rsqrtf(ss * (1.f / 128.f) + qe.eps);
     const T* g = reinterpret_cast<const T*>(kind == 0 ? qe.gq : qe.gk);
+    const float gs = rs * (kind == 0 ? qe.q_scale : 1.f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= rs * to_f32<T>(g[j * 8 + e]);
+    for (int e = 0; e < 8; ++e) v[e] *= gs * to_f32<T>(g[j * 8 + e]);
     // RoPE: column c pairs with c + 64, i.e. thread j with j ^ 8 (DPP row_ror:8).
     const int pos = qe.positions[r];
 #pragma unroll

@@ -10,6 +10,10 @@ typedef uint16_t bf16_t;
 
 // Epilogue of the fused q/k/v projection: per-head RMSNorm of q and k with
 // their gains, RoPE on q and k, then q to `q_out` and k/v into the caches.
+// log2(e) / sqrt(d_head): softmax(q.k / sqrt(d)) = 2^(q'.k - max) / sum with
+// q' = q * kScoreScaleLog2, so the attention kernels use the hardware exp2.
+constexpr float kScoreScaleLog2 = 0.1275174308f;
+
 struct QkvEpilogue {
   void* q_out;               // [rows, n_q*128]
   void* k_cache;             // [seqs, n_kv, cap, 128]
@@ -23,6 +27,8 @@ struct QkvEpilogue {
   int rows_per_seq;          // prefill: T (slot = row % T); decode: 1
   int decode;                // 1: cache slot = positions[row]
   float eps;
+  float q_scale;             // q~ is stored times this (log2(e) / sqrt(d_head): the
+                             // attention kernels then take exp2 of raw dot products)
 };
 
 // cs[row][i] = (cos, sin)(positions[row] * omega_i), i < 64, with omega_i / (2 pi)

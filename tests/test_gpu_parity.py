@@ -7,6 +7,7 @@ oracle computes one by one.  Pass bar: fp32 max abs <= 1e-4; bf16 max abs <=
 2e-2 and relative L2 <= 1e-2.
 """
 import dataclasses
+import math
 
 import numpy as np
 import pytest
@@ -27,6 +28,9 @@ def _gpu(built_lib):
     torch.cuda.synchronize()
 
 
+Q_WS_SCALE = float(np.float32(math.log2(math.e) / math.sqrt(128.0)))
+
+
 def run_prefill_gpu(w, inp, B, T, *, cap_extra=64):
     import torch
     blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
@@ -40,7 +44,8 @@ def run_prefill_gpu(w, inp, B, T, *, cap_extra=64):
     torch.cuda.synchronize()
     es = 4 if w.dtype == "f32" else 2
     qt = ws[: B * T * w.n_q * 128 * es].view(x.dtype).view(B, T, w.n_q, 128)
-    out = dict(Y=host(y), Kc=host(kc), Vc=host(vc), Q=host(qt))
+    # The workspace holds q~ times log2(e)/sqrt(d_head) (fp32 factor).
+    out = dict(Y=host(y), Kc=host(kc), Vc=host(vc), Q=host(qt) / Q_WS_SCALE)
     blk.close()
     return out
 
@@ -115,6 +120,20 @@ def test_prefill_mha_case():
     got = run_prefill_gpu(w, inp, 1, 150)
     ref = oracle_prefill(inp, w)
     assert_close(got["Y"], ref["Y"], w.dtype, "Y (MHA)")
+
+
+@pytest.mark.parametrize("n_q,n_kv,T", [(24, 8, 300), (40, 8, 190), (12, 4, 77)])
+def test_prefill_odd_group_sizes(n_q, n_kv, T):
+    # n_rep = 3 and 5: a wave's 32 packed rows cover a token range that is
+    # not aligned to the 64-key tiles.
+    w = dataclasses.replace(WORKLOADS[2], n_q=n_q, n_kv=n_kv)
+    say(f"prefill parity: n_q={n_q} n_kv={n_kv} T={T}")
+    inp = prefill_inputs(w, B=1, T=T)
+    got = run_prefill_gpu(w, inp, 1, T)
+    ref = oracle_prefill(inp, w)
+    assert_close(got["Q"], ref["Q"], w.dtype, "q~")
+    assert_close(got["Kc"][:, :, :T], ref["Kc"], w.dtype, "k cache")
+    assert_close(got["Y"], ref["Y"], w.dtype, "Y")
 
 
 def test_prefill_nonzero_positions():
