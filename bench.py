@@ -26,6 +26,102 @@ METRIC = "attention-block tokens/s and TFLOP/s (% MFMA/HBM peak), 0.6B-shape B=2
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
 
+# Measured HBM traffic of the roofline kernels (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+# calibrated on a plain copy), written by --summarize-pmc; used only while the
+# kernel sources still hash to the value recorded with it.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_B2_T2048_decode_N64.txt")
+CSRC = os.path.join(ROOT, "qwen3_gqa_attention_amd", "csrc")
+COPY_BYTES = 512 << 20        # bytes read (and written) by one calibration copy
+PMC_KERNELS = {               # roofline entry -> kernel-name substrings summed per launch
+    "prefill_attention": ["flash_prefill_kernel"],
+    "decode_attention": ["decode_attn_kernel", "decode_combine_kernel"],
+}
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """Per-launch HBM bytes of the roofline kernels, or {} if absent / stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = [l for l in f if l.startswith("TRAFFIC_JSON ")]
+        rec = json.loads(lines[-1][len("TRAFFIC_JSON "):])
+    except (OSError, IndexError, ValueError):
+        return {}
+    if rec.get("source_hash") != kernel_source_hash():
+        return {}
+    return rec.get("bytes_per_launch", {})
+
+
+def copy_calibration():
+    """A plain device copy of known size (the PMC runs scale their counters by it)."""
+    import torch
+    n = COPY_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def summarize_pmc(fetch_csv, write_csv, commands):
+    """Turn two rocprofv3 counter CSVs into the traffic file."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def avg(vals, subs):
+        tot = 0.0
+        for sub in subs:
+            ks = [k for k in vals if sub in k]
+            if not ks:
+                raise SystemExit(f"no dispatches of {sub} in the counter CSV")
+            tot += statistics.mean(v for k in ks for v in vals[k])
+        return tot
+
+    copy_kib = COPY_BYTES / 1024
+    cf, cw = avg(fetch, ["neg_kernel"]), avg(write, ["neg_kernel"])
+    sf, sw = copy_kib / cf, copy_kib / cw
+    out = {}
+    lines = ["HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
+             "each scaled by what the counter reads for a plain copy of known size",
+             f"(torch.neg over {COPY_BYTES >> 20} MiB of bf16: {copy_kib:.0f} KiB read, {copy_kib:.0f} KiB written).",
+             "", "Commands (from /tmp, TMPDIR=/tmp, one MI355X):"] + [f"    {c}" for c in commands] + [
+             "", f"copy kernel: FETCH_SIZE {cf:.0f} KiB -> fetch scale {sf:.4f}; "
+                 f"WRITE_SIZE {cw:.0f} KiB -> write scale {sw:.4f}", "",
+             "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled traffic (MB) |", "|---|---|---|---|"]
+    for key, subs in PMC_KERNELS.items():
+        f_, w_ = avg(fetch, subs), avg(write, subs)
+        b = (f_ * sf + w_ * sw) * 1024
+        out[key] = b
+        lines.append(f"| {key} ({' + '.join(subs)}) | {f_:.0f} | {w_:.0f} | {b / 1e6:.2f} |")
+    rec = {"source_hash": kernel_source_hash(), "bytes_per_launch": out,
+           "copy_scale": {"fetch": sf, "write": sw}}
+    lines += ["", "TRAFFIC_JSON " + json.dumps(rec)]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -180,7 +276,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain copy of known size (for PMC traffic calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic file from two rocprofv3 counter CSVs and exit")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="command line recorded in the traffic file (repeatable)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.pmc_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -194,6 +299,9 @@ def main():
         build()
     torch.cuda.set_device(0)
 
+    if args.copy_calibration:
+        copy_calibration()
+    traffic = load_traffic()
     log("bench: prefill 0.6B-shape B=2 T=2048 bf16")
     p = bench_prefill(args)
     log(f"bench: prefill {p['step_s'] * 1e3:.4f} ms/step; kernels " +
@@ -214,7 +322,7 @@ def main():
                          "achieved": dd["attn_bytes"] / (dd["attn_ms"] / 1e3) / 1e9,
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                          "frac": dd["attn_bytes"] / (dd["attn_ms"] / 1e3) / PEAK_HBM_BYTES,
-                         "traffic": None},
+                         "traffic": traffic.get("decode_attention")},
         }
     cpu = None
     if not args.no_cpu_baseline:
@@ -247,7 +355,7 @@ def main():
                      "achieved": p["flops"][dom] / (dk["avg_ms"] / 1e3) / 1e12,
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": p["flops"][dom] / (dk["avg_ms"] / 1e3) / PEAK_BF16_FLOPS,
-                     "traffic": None},
+                     "traffic": traffic.get("prefill_attention") if dom == "attention" else None},
         "decode": dec,
         "cpu_baseline": cpu,
     }
