@@ -223,19 +223,37 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
         if constexpr (VT) return k_off[ks];
         else return c32 * LDK + ks * MF::K + hk * MF::KL;
       };
-      typename MF::frag kf[2][NKB];
+      // K fragments are read KPF steps ahead of their MFMAs (a ring of KPF+1
+      // register sets): one step's NKB MFMAs are shorter than an LDS read.
+      constexpr int KPF = VT ? 3 : 1;
+      typename MF::frag kf[KPF + 1][NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) kf[0][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(0));
+      for (int p = 0; p < KPF; ++p)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) kf[p][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(p));
+      // The scheduler would sink the reads next to their MFMAs; pin the
+      // order: the prologue reads first, then each MFMA followed by one read
+      // KPF steps ahead.
+      __builtin_amdgcn_sched_group_barrier(0x100, KPF * NKB, 0);
 #pragma unroll
       for (int ks = 0; ks < DSTEPS; ++ks) {
-        if (ks + 1 < DSTEPS) {
+        if (ks + KPF < DSTEPS) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            kf[(ks + 1) & 1][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(ks + 1));
+            kf[(ks + KPF) % (KPF + 1)][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(ks + KPF));
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          s[kb] = MF::run(kf[ks & 1][kb], qf[ks], ks == 0 ? mbias : s[kb]);
+          s[kb] = MF::run(kf[ks % (KPF + 1)][kb], qf[ks], ks == 0 ? mbias : s[kb]);
+        if (ks + KPF < DSTEPS) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, NKB, 0);
+        }
       }
       // causal mask (only tiles that cross this wave's diagonal), running max
       if (kt * BN + BN - 1 > w_tok_lo) {
