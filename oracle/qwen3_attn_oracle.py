@@ -206,6 +206,34 @@ def decode(x, wq, wk, wv, wo, gq, gk, positions, k_cache, v_cache, *, n_q, n_kv,
     return dict(Y=Y, k_new=k[:, 0], v_new=v[:, 0], A=A, Q=q[:, 0])
 
 
+def prefill_chunk(x, wq, wk, wv, wo, gq, gk, positions, past_len, k_cache, v_cache, *,
+                  n_q, n_kv, dh=128, eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+    """A chunk of T new tokens per sequence appended to a non-empty cache.
+
+    x: [B, T, d]; positions: [B, T]; past_len[b] = P_b cached tokens;
+    k_cache, v_cache: [B, n_kv, >=P_b, dh] holding post-norm post-RoPE keys
+    and values of the first P_b tokens.  The KV cache appends the chunk's keys
+    and values after them, and chunk token t (key P_b + t) sees keys
+    0 .. P_b + t: gqa_attention with S = P_b + T ([BUILD] "The complete code":
+    KVCache.update, then the tril(diagonal=S-T) mask).  Returns Y [B, T, d],
+    Q [B, T, n_q, dh], the chunk's Kc / Vc [B, n_kv, T, dh] (cache layout) and
+    A [B, T, n_q*dh].
+    """
+    q, k, v = project_norm_rope(x, wq, wk, wv, gq, gk, positions, n_q=n_q,
+                                n_kv=n_kv, dh=dh, eps=eps, theta=theta, dtype=dtype)
+    B = q.shape[0]
+    out = []
+    for b in range(B):
+        P = int(past_len[b])
+        ks = np.concatenate([np.asarray(k_cache[b][:, :P], dtype).transpose(1, 0, 2), k[b]], axis=0)
+        vs = np.concatenate([np.asarray(v_cache[b][:, :P], dtype).transpose(1, 0, 2), v[b]], axis=0)
+        out.append(gqa_attention(q[b], ks, vs))
+    A = merge_heads(np.stack(out))
+    Y = linear(A, wo, dtype)
+    return dict(Y=Y, Q=q, Kc=np.transpose(k, (0, 2, 1, 3)),
+                Vc=np.transpose(v, (0, 2, 1, 3)), A=A)
+
+
 def prefill_rows(x, wq, wk, wv, wo, gq, gk, positions, rows, *, n_q, n_kv, dh=128,
                  eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
     """The prefill output at selected tokens only, for full-size checks.

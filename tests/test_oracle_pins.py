@@ -299,6 +299,55 @@ def test_decode_equals_last_prefill_row():
     np.testing.assert_allclose(dec["v_new"], full["Vc"][:, :, 8], rtol=1e-13, atol=1e-14)
 
 
+def chunk_args(p, lo, hi, past, kc, vc):
+    return dict(x=p["x"][:, lo:hi], wq=p["wq"], wk=p["wk"], wv=p["wv"], wo=p["wo"], gq=p["gq"],
+                gk=p["gk"], positions=p["positions"][:, lo:hi], past_len=past, k_cache=kc,
+                v_cache=vc, n_q=p["n_q"], n_kv=p["n_kv"], dh=p["dh"])
+
+
+def test_chunked_prefill_equals_one_shot_prefill():
+    # Prefilling tokens 0..P-1, then appending tokens P..P+T-1 as a chunk over
+    # that cache, gives the same outputs and cache rows as one prefill of all
+    # P+T tokens (Assembling a large model, "The complete code": KVCache
+    # concatenates after the cached keys; tril(diagonal=S-T) with S = P+T).
+    p = rand_block(21, B=2, T=14)
+    full = run_prefill(p)
+    for P in (1, 5, 9):
+        head = run_prefill({**p, "x": p["x"][:, :P], "positions": p["positions"][:, :P]})
+        ch = oracle.prefill_chunk(**chunk_args(p, P, 14, [P, P], head["Kc"], head["Vc"]))
+        np.testing.assert_allclose(ch["Y"], full["Y"][:, P:], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ch["Kc"], full["Kc"][:, :, P:], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(ch["Vc"], full["Vc"][:, :, P:], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(ch["Q"], full["Q"][:, P:], rtol=1e-13, atol=1e-14)
+
+
+def test_chunked_prefill_ragged_past_and_special_cases():
+    # Different cached lengths per sequence are independent; P = 0 is the
+    # plain prefill; a one-token chunk is a decode step.
+    p = rand_block(22, B=3, T=10)
+    past = [0, 3, 6]
+    fulls = [run_prefill({**p, "x": p["x"][b:b + 1, :past[b] + 4],
+                          "positions": p["positions"][b:b + 1, :past[b] + 4]}) for b in range(3)]
+    kc = np.full((3, p["n_kv"], 12, 16), np.nan)
+    vc = np.full_like(kc, np.nan)          # slots >= past must not be read
+    for b, P in enumerate(past):
+        kc[b, :, :P] = fulls[b]["Kc"][0, :, :P]
+        vc[b, :, :P] = fulls[b]["Vc"][0, :, :P]
+    x = np.stack([p["x"][b, past[b]:past[b] + 4] for b in range(3)])
+    pos = np.stack([p["positions"][b, past[b]:past[b] + 4] for b in range(3)])
+    ch = oracle.prefill_chunk(x, p["wq"], p["wk"], p["wv"], p["wo"], p["gq"], p["gk"], pos, past,
+                              kc, vc, n_q=p["n_q"], n_kv=p["n_kv"], dh=16)
+    for b, P in enumerate(past):
+        np.testing.assert_allclose(ch["Y"][b], fulls[b]["Y"][0, P:P + 4], rtol=1e-12, atol=1e-13)
+    one = oracle.prefill_chunk(x[:, :1], p["wq"], p["wk"], p["wv"], p["wo"], p["gq"], p["gk"],
+                               pos[:, :1], past, kc, vc, n_q=p["n_q"], n_kv=p["n_kv"], dh=16)
+    dec = oracle.decode(x[:, 0], p["wq"], p["wk"], p["wv"], p["wo"], p["gq"], p["gk"],
+                        np.array(past), kc, vc, n_q=p["n_q"], n_kv=p["n_kv"], dh=16)
+    np.testing.assert_allclose(one["Y"][:, 0], dec["Y"], rtol=1e-12, atol=1e-13)
+    zero = oracle.prefill_chunk(**chunk_args(p, 0, 10, [0, 0, 0], kc, vc))
+    np.testing.assert_allclose(zero["Y"], run_prefill(p)["Y"], rtol=1e-12, atol=1e-13)
+
+
 def test_decode_ragged_lengths_and_empty_cache():
     # Sequences with different cache lengths, including 0, are independent.
     p = rand_block(16, B=3, T=6)
