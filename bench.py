@@ -202,6 +202,70 @@ def bench_prefill(args):
                 dominant=dom, flops=flops, total_flops=total_flops, ncalls=ncalls)
 
 
+def chunk_flops(B, T, P, d, n_q, n_kv, dh=128):
+    """Algorithmic FLOPs per kernel of one chunked-prefill call (T new tokens
+    over P cached ones: token t sees P + t + 1 keys)."""
+    M = B * T
+    return {
+        "qkv_norm_rope_gemm": 2.0 * M * (n_q + 2 * n_kv) * dh * d,
+        "attention": 4.0 * B * n_q * dh * (T * P + T * (T + 1) / 2),
+        "o_proj_gemm": 2.0 * M * d * n_q * dh,
+    }
+
+
+def bench_chunk(args, P=1536, T=512):
+    """Chunked prefill: the 0.6B shape, B=2, a T-token chunk over P cached tokens."""
+    import numpy as np
+    import torch
+
+    import qwen3_gqa_attention_amd as q3
+    from workloads import EPS, ROPE_THETA, WORKLOADS, prefill_inputs
+
+    w = WORKLOADS[2]
+    B = w.B
+    inp = prefill_inputs(w, B=B, T=T)
+    bf = torch.bfloat16
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(bf)
+    blk = q3.Qwen3Attention(d(inp["Wq"]), d(inp["Wk"]), d(inp["Wv"]), d(inp["Wo"]), d(inp["gq"]),
+                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA)
+    x = d(inp["X"])
+    pos = (torch.arange(T, dtype=torch.int32, device="cuda") + P).repeat(B, 1).contiguous()
+    past = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 1)
+    kc = torch.randn((B, w.n_kv, P + T, 128), generator=gen, device="cuda").to(bf)
+    vc = torch.randn((B, w.n_kv, P + T, 128), generator=gen, device="cuda").to(bf)
+    out = torch.empty_like(x)
+    ws = torch.empty(blk.workspace_size(False, B, T), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        blk.prefill_chunk(x, pos, past, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.prefill_chunk(x, pos, past, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    blk.enable_stage_timing(args.steps)
+    for _ in range(args.steps):
+        blk.prefill_chunk(x, pos, past, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    stage_ms, ncalls = blk.stage_times()
+    blk.enable_stage_timing(0)
+    blk.close()
+    step_s = (t1 - t0) / args.steps
+    flops = chunk_flops(B, T, P, w.d, w.n_q, w.n_kv)
+    kernels = {}
+    for name, tot in zip(q3.STAGES, stage_ms):
+        avg = tot / max(ncalls, 1) / 1e3
+        kernels[name] = {"avg_ms": avg * 1e3, "tflops": flops[name] / avg / 1e12,
+                         "frac_mfma_peak": flops[name] / avg / PEAK_BF16_FLOPS}
+    total = sum(flops.values())
+    return {"workload": f"{w.name}-chunk-T{T}-past{P}", "B": B, "T": T, "past": P,
+            "ms_per_step": step_s * 1e3, "tokens_per_s": B * T / step_s,
+            "tflops": total / step_s / 1e12, "frac_mfma_peak": total / step_s / PEAK_BF16_FLOPS,
+            "kernels": kernels}
+
+
 def bench_decode(args):
     import numpy as np
     import torch
@@ -322,6 +386,10 @@ def main():
     p = bench_prefill(args)
     log(f"bench: prefill {p['step_s'] * 1e3:.4f} ms/step; kernels " +
         ", ".join(f"{k} {v['avg_ms']:.4f} ms" for k, v in p["kernels"].items()))
+    log("bench: chunked prefill 0.6B-shape B=2, 512 tokens over 1536 cached")
+    chunk = bench_chunk(args)
+    log(f"bench: chunked prefill {chunk['ms_per_step']:.4f} ms/step, "
+        f"{chunk['frac_mfma_peak'] * 100:.1f}% of MFMA peak")
     dec = None
     if not args.no_decode:
         log("bench: decode 64 sequences, caches 1024..32768")
@@ -373,6 +441,7 @@ def main():
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": p["flops"][dom] / (dk["avg_ms"] / 1e3) / PEAK_BF16_FLOPS,
                      "traffic": traffic.get("prefill_attention") if dom == "attention" else None},
+        "chunked_prefill": chunk,
         "decode": dec,
         "cpu_baseline": cpu,
     }

@@ -121,6 +121,34 @@ qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden
                                              void* workspace, size_t workspace_bytes,
                                              void* stream);
 
+/* Chunked prefill: B sequences each append T new tokens to caches that
+ * already hold past_len[b] tokens ("Assembling a large model from scratch",
+ * section "The complete code": the KVCache concatenates the new keys and
+ * values after the cached ones, and the mask is tril(diagonal = S - T) with
+ * S = past_len[b] + T keys).
+ *   hidden    [B, T, d_model]
+ *   positions [B, T] int32, drives RoPE only (typically past_len[b] + t)
+ *   past_len  [B] int32 DEVICE array: cached tokens of sequence b before this
+ *             chunk.  Precondition (not checked, device data):
+ *             0 <= past_len[b] and past_len[b] + T <= cache_cap.
+ *   k_cache, v_cache [B, n_kv, cache_cap, d_head]: slots 0..past_len[b]-1
+ *             are read; chunk token t's post-norm, post-RoPE key and its
+ *             value are written to slot past_len[b] + t, and it attends to
+ *             slots 0..past_len[b] + t.  Other slots are not touched.
+ *   out       [B, T, d_model]
+ * Same workspace size and layout as qwen3_attn_forward_prefill with the
+ * same B and T; qwen3_attn_forward_prefill is this call with every
+ * past_len[b] = 0.  EINVAL if past_len is NULL or for the argument errors of
+ * qwen3_attn_forward_prefill. */
+qwen3_attn_status qwen3_attn_forward_prefill_chunk(qwen3_attn_t* h, const void* hidden,
+                                                   const int32_t* positions,
+                                                   const int32_t* past_len,
+                                                   void* k_cache, void* v_cache,
+                                                   int64_t cache_cap, void* out,
+                                                   int32_t B, int32_t T,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   void* stream);
+
 /* Decode: one new token for each of N sequences.
  *   hidden    [N, d_model]
  *   positions [N] int32 device array, positions[s] = L_s = the number of

@@ -20,7 +20,7 @@ QWEN3_ATTN_F32 = 0
 QWEN3_ATTN_BF16 = 1
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EWORKSPACE", 5: "EHIP"}
 EXPORTED = ("qwen3_attn_create", "qwen3_attn_workspace_size", "qwen3_attn_forward_prefill",
-            "qwen3_attn_forward_decode", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
+            "qwen3_attn_forward_prefill_chunk", "qwen3_attn_forward_decode", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
             "qwen3_attn_stage_times", "qwen3_attn_status_string")
 STAGES = ("qkv_norm_rope_gemm", "attention", "o_proj_gemm")
 
@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.qwen3_attn_workspace_size.restype = sz
         L.qwen3_attn_forward_prefill.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, sz, vp]
         L.qwen3_attn_forward_prefill.restype = ctypes.c_int
+        L.qwen3_attn_forward_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i32, i32,
+                                                       vp, sz, vp]
+        L.qwen3_attn_forward_prefill_chunk.restype = ctypes.c_int
         L.qwen3_attn_forward_decode.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, vp]
         L.qwen3_attn_forward_decode.restype = ctypes.c_int
         L.qwen3_attn_destroy.argtypes = [vp]
@@ -97,6 +100,14 @@ def qwen3_attn_forward_prefill(handle, hidden, positions, k_cache, v_cache, cach
                                workspace, workspace_bytes, stream) -> int:
     return lib().qwen3_attn_forward_prefill(handle, hidden, positions, k_cache, v_cache, cache_cap,
                                             out, B, T, workspace, workspace_bytes, stream)
+
+
+def qwen3_attn_forward_prefill_chunk(handle, hidden, positions, past_len, k_cache, v_cache,
+                                     cache_cap, out, B, T, workspace, workspace_bytes,
+                                     stream) -> int:
+    return lib().qwen3_attn_forward_prefill_chunk(handle, hidden, positions, past_len, k_cache,
+                                                  v_cache, cache_cap, out, B, T, workspace,
+                                                  workspace_bytes, stream)
 
 
 def qwen3_attn_forward_decode(handle, hidden, positions, k_cache, v_cache, cache_cap, out, N,
@@ -222,6 +233,28 @@ class Qwen3Attention:
             torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise Qwen3AttnError("qwen3_attn_forward_prefill", st)
+        return out
+
+    def prefill_chunk(self, hidden, positions, past_len, k_cache, v_cache, out=None,
+                      workspace=None):
+        """hidden [B,T,d]; positions [B,T] int32; past_len [B] int32 (device) = tokens
+        already cached per sequence; caches [B,n_kv,cap,128] (slots past..past+T-1 written)."""
+        torch = _torch()
+        B, T, d = hidden.shape
+        cap = k_cache.shape[2]
+        if out is None:
+            out = torch.empty_like(hidden)
+        nbytes = self.workspace_size(False, B, T)
+        ws = self._workspace(nbytes, workspace)
+        st = qwen3_attn_forward_prefill_chunk(
+            self.handle, _ptr(hidden, "hidden", self.dtype), _ptr(positions, "positions", torch.int32, (B, T)),
+            _ptr(past_len, "past_len", torch.int32, (B,)),
+            _ptr(k_cache, "k_cache", self.dtype, (B, self.n_kv, cap, self.d_head)),
+            _ptr(v_cache, "v_cache", self.dtype, (B, self.n_kv, cap, self.d_head)), cap,
+            _ptr(out, "out", self.dtype, (B, T, d)), B, T, _ptr(ws, "workspace"), ws.numel() * ws.element_size(),
+            torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise Qwen3AttnError("qwen3_attn_forward_prefill_chunk", st)
         return out
 
     def decode(self, hidden, positions, k_cache, v_cache, out=None, workspace=None):

@@ -128,8 +128,9 @@ qwen3_attn_status hip_status(hipError_t e) {
 
 template <typename T>
 qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
-                              void* k_cache, void* v_cache, int64_t cap, void* out, int B,
-                              int T_len, char* ws, const WsLayout& L, hipStream_t s) {
+                              const int32_t* past, void* k_cache, void* v_cache, int64_t cap,
+                              void* out, int B, int T_len, char* ws, const WsLayout& L,
+                              hipStream_t s) {
   const qwen3_attn_desc& d = h->desc;
   const int M = B * T_len;
   const int nqkv = (d.n_q + 2 * d.n_kv) * 128;
@@ -138,7 +139,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
-                    d.n_q, d.n_kv, cap, T_len, 0, d.eps, q3::kScoreScaleLog2};
+                    d.n_q, d.n_kv, cap, T_len, 0, d.eps, past, q3::kScoreScaleLog2};
   mark(h, s, 0);
   hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, M, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
@@ -149,7 +150,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   mark(h, s, 1);
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                   reinterpret_cast<const T*>(v_cache), abuf, B, T_len, d.n_q, d.n_kv,
-                                  cap, s);
+                                  cap, past, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
@@ -169,7 +170,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
-                    d.n_q, d.n_kv, cap, 1, 1, d.eps, q3::kScoreScaleLog2};
+                    d.n_q, d.n_kv, cap, 1, 1, d.eps, nullptr, q3::kScoreScaleLog2};
   mark(h, s, 0);
   float* part = L.part ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
   hipError_t r = hipSuccess;
@@ -275,14 +276,14 @@ size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
   return L.total;
 }
 
-qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,
-                                             const int32_t* positions, void* k_cache,
-                                             void* v_cache, int64_t cache_cap, void* out,
-                                             int32_t B, int32_t T, void* workspace,
-                                             size_t workspace_bytes, void* stream) {
+namespace {
+qwen3_attn_status prefill_entry(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
+                                const int32_t* past, void* k_cache, void* v_cache,
+                                int64_t cache_cap, void* out, int32_t B, int32_t T,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   if (!h || !hidden || !positions || !k_cache || !v_cache || !out) return QWEN3_ATTN_EINVAL;
   if (B <= 0 || T <= 0 || cache_cap <= 0 || T > cache_cap) return QWEN3_ATTN_EINVAL;
-  if (B > 65535) return QWEN3_ATTN_EUNSUPPORTED;
+  if (B > 65535 || cache_cap > INT_MAX) return QWEN3_ATTN_EUNSUPPORTED;
   WsLayout L;
   if (!ws_layout(&h->desc, 0, B, T, cache_cap, &L)) return QWEN3_ATTN_EUNSUPPORTED;
   if (!workspace || workspace_bytes < L.total) return QWEN3_ATTN_EWORKSPACE;
@@ -291,10 +292,31 @@ qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (h->desc.dtype == QWEN3_ATTN_F32)
-    return run_prefill<float>(h, hidden, positions, k_cache, v_cache, cache_cap, out, B, T, ws, L,
-                              s);
-  return run_prefill<q3::bf16_t>(h, hidden, positions, k_cache, v_cache, cache_cap, out, B, T, ws,
-                                 L, s);
+    return run_prefill<float>(h, hidden, positions, past, k_cache, v_cache, cache_cap, out, B, T,
+                              ws, L, s);
+  return run_prefill<q3::bf16_t>(h, hidden, positions, past, k_cache, v_cache, cache_cap, out, B,
+                                 T, ws, L, s);
+}
+}  // namespace
+
+qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,
+                                             const int32_t* positions, void* k_cache,
+                                             void* v_cache, int64_t cache_cap, void* out,
+                                             int32_t B, int32_t T, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return prefill_entry(h, hidden, positions, nullptr, k_cache, v_cache, cache_cap, out, B, T,
+                       workspace, workspace_bytes, stream);
+}
+
+qwen3_attn_status qwen3_attn_forward_prefill_chunk(qwen3_attn_t* h, const void* hidden,
+                                                   const int32_t* positions,
+                                                   const int32_t* past_len, void* k_cache,
+                                                   void* v_cache, int64_t cache_cap, void* out,
+                                                   int32_t B, int32_t T, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  if (!past_len) return QWEN3_ATTN_EINVAL;
+  return prefill_entry(h, hidden, positions, past_len, k_cache, v_cache, cache_cap, out, B, T,
+                       workspace, workspace_bytes, stream);
 }
 
 qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,

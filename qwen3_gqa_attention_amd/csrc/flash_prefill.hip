@@ -56,7 +56,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc,
                                                             T* __restrict__ Out, int B, int T_len,
-                                                            int n_q, int n_kv, int64_t cap) {
+                                                            int n_q, int n_kv, int64_t cap,
+                                                            const int32_t* __restrict__ past) {
   using MF = Mfma32<T>;
   constexpr int BN = FlashTile<T>::BN;
   constexpr int NKB = BN / 32;                 // 32-key blocks per tile
@@ -89,6 +90,10 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // ones fill CUs as they free up.
   const int qt = tiles_per_group - 1 - blockIdx.x / groups;
   const int b = bg / n_kv, g = bg % n_kv;
+  // Chunked prefill: the sequence already holds P cached tokens, chunk token
+  // t is key P + t and sees keys 0 .. P + t (P = 0 for a first prefill).
+  const int P = past ? past[b] : 0;
+  const int S_len = P + T_len;
 
   // Wave w owns query block w & 3 (32 rows) over key half w >> 2 (with
   // KSPLIT = 2; with KSPLIT = 1 four waves cover the whole key range).
@@ -102,18 +107,19 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int Rw = R0 + qblk * 32;
   const int Rl = Rw + c32;
   const bool row_ok = Rl < rows_total;
-  const int tok = row_ok ? Rl / n_rep : T_len - 1;
+  const int qtok = row_ok ? Rl / n_rep : T_len - 1;   // token inside the chunk
+  const int tok = P + qtok;                            // its key position
   const int head = g * n_rep + (row_ok ? Rl % n_rep : 0);
   const bool wave_active = Rw < rows_total;
-  const int w_tok_lo = min(Rw, rows_total - 1) / n_rep;
-  const int w_tok_hi = min(Rw + 31, rows_total - 1) / n_rep;
-  const int kmax = min(R0 + 127, rows_total - 1) / n_rep;
+  const int w_tok_lo = P + min(Rw, rows_total - 1) / n_rep;
+  const int w_tok_hi = P + min(Rw + 31, rows_total - 1) / n_rep;
+  const int kmax = P + min(R0 + 127, rows_total - 1) / n_rep;
   const int ntiles = kmax / BN + 1;
 
   // Q^T fragments for the whole d_head, kept in VGPRs.
   typename MF::frag qf[DSTEPS];
   {
-    const T* qrow = Q + ((size_t)(b * T_len + tok) * n_q + head) * kHeadDim + hk * MF::KL;
+    const T* qrow = Q + ((size_t)(b * T_len + qtok) * n_q + head) * kHeadDim + hk * MF::KL;
 #pragma unroll
     for (int ks = 0; ks < DSTEPS; ++ks) qf[ks] = row_ok ? MF::load(qrow + ks * MF::K) : MF::zero();
   }
@@ -144,10 +150,10 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     const int kbase = kt * BN;
     const uint32_t lk = smem_lds + (uint32_t)((Ks(buf) - smem) * sizeof(T));
     const uint32_t lv = smem_lds + (uint32_t)((Vs(buf) - smem) * sizeof(T));
-    const bool full = kbase + BN <= T_len;  // uniform
+    const bool full = kbase + BN <= S_len;  // uniform
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int key = full ? kbase + dma_row[j] : min(kbase + dma_row[j], T_len - 1);
+      const int key = full ? kbase + dma_row[j] : min(kbase + dma_row[j], S_len - 1);
       const T* krow = Kg + (size_t)key * kHeadDim;
       const T* vrow = Vg + (size_t)key * kHeadDim;
       const uint32_t r4b = (uint32_t)((j * 4 + hw) * 4 * LDK * sizeof(T));  // this instruction's first row
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     for (int i = 0; i < RCH; ++i) {
       const int c = th + i * 256, key = c >> 5, cc = c & 31;
       const size_t off = (size_t)(kbase + key) * kHeadDim + cc * EPC;
-      const bool ok = kbase + key < T_len;
+      const bool ok = kbase + key < S_len;
       rkA[i] = ok ? ld16(Kg + off) : u32x4_v{0u, 0u, 0u, 0u};
       rvA[i] = ok ? ld16(Vg + off) : u32x4_v{0u, 0u, 0u, 0u};
     }
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   if (!row_ok) return;
   l_run += __shfl_xor(l_run, 32, kWave);
   const float inv = 1.f / l_run;
-  T* orow = Out + ((size_t)(b * T_len + tok) * n_q + head) * kHeadDim;
+  T* orow = Out + ((size_t)(b * T_len + qtok) * n_q + head) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -436,7 +442,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
 
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
-                                int n_q, int n_kv, int64_t cap, hipStream_t s) {
+                                int n_q, int n_kv, int64_t cap, const int32_t* past,
+                                hipStream_t s) {
   const int n_rep = n_q / n_kv;
   const int tiles = (T_len * n_rep + 127) / 128;
   // Few query tiles: split each tile's key range over two wave groups so both
@@ -445,16 +452,18 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
   const int wgs = tiles * B * n_kv;
   if (wgs < 4 * 256)
     hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, cap);
+                       T_len, n_q, n_kv, cap, past);
   else
     hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, cap);
+                       T_len, n_q, n_kv, cap, past);
   return hipGetLastError();
 }
 
 template hipError_t launch_flash_prefill<float>(const float*, const float*, const float*, float*,
-                                                int, int, int, int, int64_t, hipStream_t);
+                                                int, int, int, int, int64_t, const int32_t*,
+                                                hipStream_t);
 template hipError_t launch_flash_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
-                                                 bf16_t*, int, int, int, int, int64_t, hipStream_t);
+                                                 bf16_t*, int, int, int, int, int64_t,
+                                                 const int32_t*, hipStream_t);
 
 }  // namespace q3

@@ -24,9 +24,11 @@ struct QkvEpilogue {
   const float2* rope_cs;     // [rows][64] (cos, sin) of position * omega_i
   int n_q, n_kv;
   int64_t cap;
-  int rows_per_seq;          // prefill: T (slot = row % T); decode: 1
+  int rows_per_seq;          // prefill: T (slot = past + row % T); decode: 1
   int decode;                // 1: cache slot = positions[row]
   float eps;
+  const int32_t* past;       // prefill: [seqs] cached tokens before this chunk (slot =
+                             // past[seq] + row % T), or null for empty caches
   float q_scale;             // q~ is stored times this (log2(e) / sqrt(d_head): the
                              // attention kernels then take exp2 of raw dot products)
 };
@@ -53,10 +55,13 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
 // fp32 scratch (floats) the split-K path of an M <= 64 projection needs.
 int small_m_partial_floats(int M, int N, int K, int elem_size);
 
-// Causal GQA flash attention over the freshly written caches.
+// Causal GQA flash attention of a T_len-token chunk over the caches, which
+// hold past[b] earlier tokens of sequence b followed by the chunk (past may
+// be null: empty caches).
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
-                                int n_q, int n_kv, int64_t cap, hipStream_t s);
+                                int n_q, int n_kv, int64_t cap, const int32_t* past,
+                                hipStream_t s);
 
 // Split-K decode attention: partial (max, sum, weighted values) per key chunk,
 // then the log-sum-exp merge into Out [N, n_q*128].

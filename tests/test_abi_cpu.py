@@ -96,6 +96,11 @@ def test_workspace_size_zero_for_invalid(built_lib, args):
 
 def test_forward_with_null_handle_is_einval(built_lib):
     assert q3.qwen3_attn_forward_prefill(None, 1, 1, 1, 1, 16, 1, 1, 8, 1, 1 << 20, None) == 1
+    # chunked prefill: a missing past_len array is rejected before the handle is used
+    assert q3.qwen3_attn_forward_prefill_chunk(1, 1, 1, None, 1, 1, 16, 1, 1, 8, 1, 1 << 20,
+                                               None) == 1
+    assert q3.qwen3_attn_forward_prefill_chunk(None, 1, 1, 1, 1, 1, 16, 1, 1, 8, 1, 1 << 20,
+                                               None) == 1
     assert q3.qwen3_attn_forward_decode(None, 1, 1, 1, 1, 16, 1, 1, 1, 1 << 20, None) == 1
     q3.qwen3_attn_destroy(None)   # NULL is a no-op
 

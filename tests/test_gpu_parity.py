@@ -164,6 +164,118 @@ def test_prefill_deterministic_and_causal():
     assert not np.array_equal(c["Y"][:, t + 1:], a["Y"][:, t + 1:])
 
 
+# ---------------------------------------------------------------- chunked prefill
+def chunk_case(idx, B, T, past, *, seed=None, cap_extra=40):
+    w = WORKLOADS[idx]
+    inp = prefill_inputs(w, B=B, T=T, seed=seed)
+    past = np.asarray(past, np.int32)
+    inp["positions"] = (past[:, None] + np.arange(T, dtype=np.int32)[None, :]).astype(np.int32)
+    cap = int(past.max()) + T + cap_extra
+    kc, vc = decode_cache_host(w, past, cap, seed=(w.seed if seed is None else seed) + 1)
+    for b, P in enumerate(past):   # slots >= past hold NaN: written or never read
+        kc[b, :, P:] = np.nan
+        vc[b, :, P:] = np.nan
+    return w, inp, past, kc, vc
+
+
+def run_chunk_gpu(w, inp, past, kc_host, vc_host):
+    import torch
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    pl = torch.from_numpy(past).to("cuda")
+    kc, vc = dev(kc_host, w.dtype), dev(vc_host, w.dtype)
+    y = blk.prefill_chunk(x, pos, pl, kc, vc)
+    torch.cuda.synchronize()
+    out = dict(Y=host(y), Kc=host(kc), Vc=host(vc))
+    blk.close()
+    return out
+
+
+def oracle_chunk(w, inp, past, kc, vc):
+    return oracle.prefill_chunk(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], inp["gq"],
+                                inp["gk"], inp["positions"], past, kc, vc, n_q=w.n_q, n_kv=w.n_kv,
+                                eps=EPS, theta=ROPE_THETA)
+
+
+CHUNK_CASES = [
+    (1, 1, 58, [70]),            # fp32, past not a multiple of the 32-key tile
+    (2, 2, 150, [37, 300]),      # 0.6B shape, ragged past lengths
+    (2, 3, 1, [0, 64, 1000]),    # one-token chunks (decode-like), incl. an empty cache
+    (3, 2, 64, [0, 129]),        # 4B shape (n_rep 4)
+    (4, 1, 65, [200]),           # wide GQA (n_rep 16)
+]
+
+
+@pytest.mark.parametrize("idx,B,T,past", CHUNK_CASES)
+def test_prefill_chunk_parity(idx, B, T, past):
+    w, inp, past, kc, vc = chunk_case(idx, B, T, past)
+    say(f"chunked prefill parity: workload {idx} ({w.name}) B={B} T={T} past={past.tolist()}")
+    got = run_chunk_gpu(w, inp, past, kc, vc)
+    ref = oracle_chunk(w, inp, past, kc, vc)
+    for b, P in enumerate(past):
+        # cached slots untouched, the chunk's slots written, the rest untouched
+        np.testing.assert_array_equal(got["Kc"][b, :, :P], kc[b, :, :P])
+        np.testing.assert_array_equal(got["Vc"][b, :, :P], vc[b, :, :P])
+        assert_close(got["Kc"][b, :, P:P + T], ref["Kc"][b], w.dtype, f"k cache chunk (seq {b})")
+        assert_close(got["Vc"][b, :, P:P + T], ref["Vc"][b], w.dtype, f"v cache chunk (seq {b})")
+        assert np.all(np.isnan(got["Kc"][b, :, P + T:])), "slots past the chunk were written"
+    assert_close(got["Y"], ref["Y"], w.dtype, "block output Y")
+
+
+def test_prefill_chunk_after_prefill_equals_one_shot():
+    # On the GPU: prefill of P tokens, then the next T tokens as a chunk over
+    # the same caches, against one prefill of all P+T tokens.
+    import torch
+    w = WORKLOADS[2]
+    P, T = 200, 137
+    inp = prefill_inputs(w, B=2, T=P + T)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    cap = P + T + 8
+    kc1 = torch.zeros((2, w.n_kv, cap, 128), dtype=x.dtype, device="cuda")
+    vc1 = torch.zeros_like(kc1)
+    y_full = blk.prefill(x, pos, kc1, vc1)
+    kc2, vc2 = torch.zeros_like(kc1), torch.zeros_like(kc1)
+    blk.prefill(x[:, :P].contiguous(), pos[:, :P].contiguous(), kc2, vc2)
+    past = torch.full((2,), P, dtype=torch.int32, device="cuda")
+    y_tail = blk.prefill_chunk(x[:, P:].contiguous(), pos[:, P:].contiguous(), past, kc2, vc2)
+    torch.cuda.synchronize()
+    assert_close(host(y_tail), host(y_full)[:, P:], w.dtype, "Y chunk vs one-shot")
+    np.testing.assert_array_equal(host(kc2), host(kc1))
+    np.testing.assert_array_equal(host(vc2), host(vc1))
+    blk.close()
+
+
+def test_prefill_chunk_full_size_0p6b():
+    # The 0.6B shape: a 512-token chunk per sequence over 1536 cached tokens.
+    w, inp, past, kc, vc = chunk_case(2, 2, 512, [1536, 1536], cap_extra=0)
+    say("chunked prefill full size: 0.6B B=2 T=512 past=1536")
+    got = run_chunk_gpu(w, inp, past, kc, vc)
+    ref = oracle_chunk(w, inp, past, kc, vc)
+    assert_close(got["Y"], ref["Y"], w.dtype, "block output Y")
+    assert_close(got["Kc"][:, :, 1536:], ref["Kc"], w.dtype, "k cache chunk")
+
+
+def test_prefill_chunk_argument_errors():
+    import torch
+    import qwen3_gqa_attention_amd as q3
+    w = WORKLOADS[2]
+    inp = prefill_inputs(w, B=1, T=8)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    kc = torch.zeros((1, w.n_kv, 16, 128), dtype=x.dtype, device="cuda")
+    ws = torch.empty(blk.workspace_size(False, 1, 8), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    st = q3.qwen3_attn_forward_prefill_chunk(blk.handle, x.data_ptr(), pos.data_ptr(), None,
+                                             kc.data_ptr(), kc.data_ptr(), 16, out.data_ptr(), 1, 8,
+                                             ws.data_ptr(), ws.numel(), None)
+    assert st == 1   # EINVAL: past_len missing
+    blk.close()
+
+
 # ------------------------------------------------------------------------- decode
 def run_decode_gpu(w, inp, kc_host, vc_host, cap):
     import torch
