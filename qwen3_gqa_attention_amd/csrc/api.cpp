@@ -67,10 +67,12 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
     L->q_off = 0;
     L->a_off = qb;
     L->cs_off = 2 * qb;
-    L->acc_off = L->ml_off = L->part_off = 0;
+    L->acc_off = L->ml_off = 0;
     L->nchunk = 0;
     L->part = false;
-    L->total = L->cs_off + align_up((size_t)n * T * 64 * 2 * sizeof(float));
+    L->part_off = L->cs_off + align_up((size_t)n * T * 64 * 2 * sizeof(float));
+    L->total = L->part_off +
+               align_up(q3::flash_partial_floats(n, T, d->n_q, d->n_kv) * sizeof(float));
     return true;
   }
   if (T != 1 || cap <= 0 || cap > INT_MAX) return false;
@@ -150,7 +152,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   mark(h, s, 1);
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                   reinterpret_cast<const T*>(v_cache), abuf, B, T_len, d.n_q, d.n_kv,
-                                  cap, past, s);
+                                  cap, past, reinterpret_cast<float*>(ws + L.part_off), s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),

@@ -57,7 +57,9 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             const T* __restrict__ Vc,
                                                             T* __restrict__ Out, int B, int T_len,
                                                             int n_q, int n_kv, int64_t cap,
-                                                            const int32_t* __restrict__ past) {
+                                                            const int32_t* __restrict__ past,
+                                                            int nsplit,
+                                                            float* __restrict__ part) {
   using MF = Mfma32<T>;
   constexpr int BN = FlashTile<T>::BN;
   constexpr int NKB = BN / 32;                 // 32-key blocks per tile
@@ -85,10 +87,18 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int rows_total = T_len * n_rep;
   const int tiles_per_group = (rows_total + 127) / 128;
   const int groups = B * n_kv;
+  // With nsplit > 1 the key range of each query tile is cut into nsplit
+  // parts run by separate workgroups (few query tiles: fill the chip); each
+  // part leaves unnormalised partial results for flash_combine_kernel.
+  // The (sequence, KV head) group varies fastest: workgroups are dealt
+  // round-robin over the 8 XCDs, so each XCD keeps serving the same groups
+  // and their K/V stay in its L2.
   const int bg = blockIdx.x % groups;
+  const int rest = blockIdx.x / groups;
+  const int split = rest % nsplit;
   // Query tiles are issued heaviest (longest key range) first, so lighter
   // ones fill CUs as they free up.
-  const int qt = tiles_per_group - 1 - blockIdx.x / groups;
+  const int qt = tiles_per_group - 1 - rest / nsplit;
   const int b = bg / n_kv, g = bg % n_kv;
   // Chunked prefill: the sequence already holds P cached tokens, chunk token
   // t is key P + t and sees keys 0 .. P + t (P = 0 for a first prefill).
@@ -114,7 +124,10 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int w_tok_lo = P + min(Rw, rows_total - 1) / n_rep;
   const int w_tok_hi = P + min(Rw + 31, rows_total - 1) / n_rep;
   const int kmax = P + min(R0 + 127, rows_total - 1) / n_rep;
-  const int ntiles = kmax / BN + 1;
+  const int ntiles_all = kmax / BN + 1;
+  const int per_split = (ntiles_all + nsplit - 1) / nsplit;
+  const int t_lo = min(split * per_split, ntiles_all);
+  const int ntiles = min(t_lo + per_split, ntiles_all) - t_lo;  // this workgroup's key tiles
 
   // Q^T fragments for the whole d_head, kept in VGPRs.
   typename MF::frag qf[DSTEPS];
@@ -363,7 +376,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // iteration earlier) is staged after it.  Both halves run n0 iterations so
   // every wave meets every barrier.
   const int n0 = KSPLIT == 2 ? (ntiles + 1) / 2 : ntiles;
-  const int base = kh ? n0 : 0;
+  const int base = t_lo + (kh ? n0 : 0);
   const int cnt = kh ? ntiles - n0 : n0;
   const int s0 = kh * 2, s1 = kh * 2 + 1;
   if constexpr (VT) {
@@ -412,6 +425,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     const float a0 = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
     const float a1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - M);
     l_run = a0 * l_run + a1 * l1;
+    m_run = M;  // O and l are now relative to the merged max (the split path writes it)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -421,6 +435,25 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
 
   if (!row_ok) return;
   l_run += __shfl_xor(l_run, 32, kWave);
+  if (nsplit > 1) {
+    // Partial results of this key range: O unnormalised, and (m, l).
+    const size_t prow = ((size_t)split * B * T_len + (size_t)b * T_len + qtok) * n_q + head;
+    float* po = part + prow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = db * 32 + 8 * i4 + 4 * hk;
+        *reinterpret_cast<f32x4_v*>(po + d) =
+            f32x4_v{o[db][i4 * 4 + 0], o[db][i4 * 4 + 1], o[db][i4 * 4 + 2], o[db][i4 * 4 + 3]};
+      }
+    if (hk == 0) {
+      float* pml = part + (size_t)nsplit * B * T_len * n_q * kHeadDim + prow * 2;
+      pml[0] = m_run;
+      pml[1] = l_run;
+    }
+    return;
+  }
   const float inv = 1.f / l_run;
   T* orow = Out + ((size_t)(b * T_len + qtok) * n_q + head) * kHeadDim;
 #pragma unroll
@@ -440,30 +473,84 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     }
 }
 
+// Merge the nsplit partial results of each (token, query head): one online
+// log-sum-exp pass over the parts, then O / l rounded to T.  32 threads per
+// (token, head), 4 dims each (16-byte loads); 8 pairs per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void flash_combine_kernel(const float* __restrict__ part,
+                                                            int nsplit, int pairs,
+                                                            T* __restrict__ Out) {
+  const int pair = blockIdx.x * 8 + (threadIdx.x >> 5), d = (threadIdx.x & 31) * 4;
+  if (pair >= pairs) return;
+  const float* pml = part + (size_t)nsplit * pairs * kHeadDim;
+  float M = -INFINITY, l = 0.f;
+  f32x4_v o = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const size_t row = (size_t)sp * pairs + pair;
+    const float m = pml[row * 2], lp = pml[row * 2 + 1];
+    const f32x4_v op = *reinterpret_cast<const f32x4_v*>(part + row * kHeadDim + d);
+    if (m == -INFINITY) continue;  // no key of this part is visible to the row
+    const float mn = fmaxf(M, m);
+    const float a = __builtin_amdgcn_exp2f(M - mn);  // 0 while M is -inf
+    const float w = __builtin_amdgcn_exp2f(m - mn);
+    l = l * a + lp * w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = o[e] * a + op[e] * w;
+    M = mn;
+  }
+  const float inv = 1.f / l;
+  T* dst = Out + (size_t)pair * kHeadDim + d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[e] * inv);
+}
+
+// Query-tile workgroups of one prefill call and the number of key splits:
+// below 256 workgroups the key ranges are split so that about 256 run.
+static int flash_query_wgs(int B, int T_len, int n_q, int n_kv) {
+  return (T_len * (n_q / n_kv) + 127) / 128 * B * n_kv;
+}
+int flash_splits(int B, int T_len, int n_q, int n_kv) {
+  const int wgs = flash_query_wgs(B, T_len, n_q, n_kv);
+  if (wgs >= 256) return 1;
+  const int sp = 256 / wgs;
+  return sp < 2 ? 2 : (sp > 8 ? 8 : sp);
+}
+size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv) {
+  const int sp = flash_splits(B, T_len, n_q, n_kv);
+  return sp > 1 ? (size_t)sp * B * T_len * n_q * (kHeadDim + 2) : 0;
+}
+
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
-                                int n_q, int n_kv, int64_t cap, const int32_t* past,
+                                int n_q, int n_kv, int64_t cap, const int32_t* past, float* part,
                                 hipStream_t s) {
-  const int n_rep = n_q / n_kv;
-  const int tiles = (T_len * n_rep + 127) / 128;
-  // Few query tiles: split each tile's key range over two wave groups so both
-  // waves of a SIMD serve the same tile.  Many tiles: 4-wave workgroups, two
-  // resident per CU.
-  const int wgs = tiles * B * n_kv;
+  const int nsplit = flash_splits(B, T_len, n_q, n_kv);
+  if (nsplit > 1 && !part) return hipErrorInvalidValue;
+  // Few workgroups: split each query tile's key range over two wave groups
+  // so both waves of a SIMD serve the same tile.  Many: 4-wave workgroups,
+  // two resident per CU.
+  const int wgs = flash_query_wgs(B, T_len, n_q, n_kv) * nsplit;
   if (wgs < 4 * 256)
     hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, cap, past);
+                       T_len, n_q, n_kv, cap, past, nsplit, part);
   else
     hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, cap, past);
+                       T_len, n_q, n_kv, cap, past, nsplit, part);
+  if (nsplit > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int pairs = B * T_len * n_q;
+    hipLaunchKernelGGL(flash_combine_kernel<T>, dim3((pairs + 7) / 8), dim3(256), 0, s, part,
+                       nsplit, pairs, Out);
+  }
   return hipGetLastError();
 }
 
 template hipError_t launch_flash_prefill<float>(const float*, const float*, const float*, float*,
                                                 int, int, int, int, int64_t, const int32_t*,
-                                                hipStream_t);
+                                                float*, hipStream_t);
 template hipError_t launch_flash_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
                                                  bf16_t*, int, int, int, int, int64_t,
-                                                 const int32_t*, hipStream_t);
+                                                 const int32_t*, float*, hipStream_t);
 
 }  // namespace q3

@@ -516,7 +516,11 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
   if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, false>(A, W, M, N, K, qe, se, s);
   if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus)
     return launch_gemm<T, 4, 2, 2, 4, false>(A, W, M, N, K, qe, se, s);
-  return launch_gemm<T, 2, 2, 2, 2, false>(A, W, M, N, K, qe, se, s);
+  if (N % 128 == 0 && ((M + 127) / 128) * (N / 128) >= kCus)
+    return launch_gemm<T, 2, 2, 2, 2, false>(A, W, M, N, K, qe, se, s);
+  // Too few 128x128 tiles to fill the chip (e.g. o_proj of a 1024-token
+  // chunk): 64x64 tiles, four 32x32 waves (N is a multiple of 64).
+  return launch_gemm<T, 2, 2, 1, 1, false>(A, W, M, N, K, qe, se, s);
 }
 
 template hipError_t launch_qkv_gemm<float>(const float*, const float*, int, int, int,

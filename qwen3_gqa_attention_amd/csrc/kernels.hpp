@@ -58,10 +58,15 @@ int small_m_partial_floats(int M, int N, int K, int elem_size);
 // Causal GQA flash attention of a T_len-token chunk over the caches, which
 // hold past[b] earlier tokens of sequence b followed by the chunk (past may
 // be null: empty caches).
+// `part`: fp32 scratch of flash_partial_floats(...) floats (may be null when
+// that is 0): with few query tiles the key ranges are split over more
+// workgroups and merged by a second kernel.
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
-                                int n_q, int n_kv, int64_t cap, const int32_t* past,
+                                int n_q, int n_kv, int64_t cap, const int32_t* past, float* part,
                                 hipStream_t s);
+int flash_splits(int B, int T_len, int n_q, int n_kv);
+size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv);
 
 // Split-K decode attention: partial (max, sum, weighted values) per key chunk,
 // then the log-sum-exp merge into Out [N, n_q*128].

@@ -74,7 +74,11 @@ def test_workspace_size_prefill_and_decode(built_lib):
     # prefill: rotated q, merged attention output, RoPE (cos, sin) table
     assert q3.qwen3_attn_workspace_size(d, 0, 2, 2048, 0) == 2 * align(2 * 2048 * 2048 * 2) + align(4096 * 64 * 8)
     d32 = desc(dtype=q3.QWEN3_ATTN_F32)
-    assert q3.qwen3_attn_workspace_size(d32, 0, 1, 128, 0) == 2 * align(128 * 2048 * 4) + align(128 * 64 * 8)
+    # B=1, T=128: 16 query-tile workgroups (< 256), so each key range is split
+    # 8 ways and the fp32 partials (O, then m and l) are reserved as well
+    part = 8 * 128 * 16 * (128 + 2) * 4
+    assert (q3.qwen3_attn_workspace_size(d32, 0, 1, 128, 0)
+            == 2 * align(128 * 2048 * 4) + align(128 * 64 * 8) + align(part))
     # decode: q and merged output, then per-chunk partials (512-key chunks)
     cap, N = 32832, 64
     nchunk = -(-cap // 512)
