@@ -321,6 +321,63 @@ def bench_decode(args):
                 attn_ms=attn_ms, attn_bytes=attn_bytes, N=w.B, mean_len=float(L.mean()), w=w)
 
 
+def bench_decode_paged(args, bs=64):
+    """Decode over a paged cache: the same 64 sequences, their keys/values in
+    64-token blocks of one pool, the blocks of all sequences shuffled."""
+    import numpy as np
+    import torch
+
+    import qwen3_gqa_attention_amd as q3
+    from workloads import EPS, ROPE_THETA, WORKLOADS, decode_inputs
+
+    w = WORKLOADS[5]
+    inp = decode_inputs(w)
+    L = inp["positions"]
+    bf = torch.bfloat16
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(bf)
+    blk = q3.Qwen3Attention(d(inp["Wq"]), d(inp["Wk"]), d(inp["Wv"]), d(inp["Wo"]), d(inp["gq"]),
+                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA)
+    need = (L.astype(np.int64) + bs) // bs          # blocks for L + 1 tokens
+    mb, nb = int(need.max()), int(need.sum())
+    perm = np.random.default_rng(w.seed + 11).permutation(nb).astype(np.int32)
+    table = np.zeros((w.B, mb), np.int32)
+    off = 0
+    for s in range(w.B):
+        table[s, : need[s]] = perm[off: off + need[s]]
+        table[s, need[s]:] = perm[off + need[s] - 1]
+        off += need[s]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 12)
+    kp = torch.empty((nb, w.n_kv, bs, 128), dtype=bf, device="cuda")
+    vp = torch.empty_like(kp)
+    for lo in range(0, nb, 4096):   # N(0,1) blocks, drawn in slices to bound the fp32 temporary
+        hi = min(nb, lo + 4096)
+        kp[lo:hi] = torch.randn((hi - lo, w.n_kv, bs, 128), generator=gen, device="cuda").to(bf)
+        vp[lo:hi] = torch.randn((hi - lo, w.n_kv, bs, 128), generator=gen, device="cuda").to(bf)
+    x = d(inp["X"])
+    pos = torch.from_numpy(L).cuda()
+    tab = torch.from_numpy(table).cuda()
+    out = torch.empty_like(x)
+    ws = torch.empty(blk.workspace_size(True, w.B, 1, mb * bs), dtype=torch.uint8, device="cuda")
+    for _ in range(max(args.warmup // 2, 2)):
+        blk.decode_paged(x, pos, tab, kp, vp, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    steps = args.decode_steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        blk.decode_paged(x, pos, tab, kp, vp, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    blk.close()
+    del kp, vp
+    torch.cuda.empty_cache()
+    nbytes = float(np.sum(L.astype(np.int64))) * 2 * w.n_kv * 128 * 2 + \
+        ((w.n_q + 2 * w.n_kv) * 128 * w.d * 2 + w.d * w.n_q * 128 * 2)
+    return {"workload": f"{w.name}-paged-bs{bs}", "block_size": bs, "blocks": nb,
+            "ms_per_step": step_s * 1e3, "tokens_per_s": w.B / step_s,
+            "GBps": nbytes / step_s / 1e9, "frac_hbm_peak": nbytes / step_s / PEAK_HBM_BYTES}
+
+
 def cpu_baseline(seconds):
     """The fp64 oracle's own code run in float32 on host cores, bounded sample."""
     import numpy as np
@@ -408,6 +465,12 @@ def main():
                          "frac": dd["attn_bytes"] / (dd["attn_ms"] / 1e3) / PEAK_HBM_BYTES,
                          "traffic": traffic.get("decode_attention")},
         }
+    dec_paged = None
+    if not args.no_decode:
+        log("bench: decode over a paged cache (64-token blocks, shuffled pool)")
+        dec_paged = bench_decode_paged(args)
+        log(f"bench: paged decode {dec_paged['ms_per_step']:.4f} ms/step, "
+            f"{dec_paged['frac_hbm_peak'] * 100:.1f}% of HBM peak")
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle, float32)")
@@ -443,6 +506,7 @@ def main():
                      "traffic": traffic.get("prefill_attention") if dom == "attention" else None},
         "chunked_prefill": chunk,
         "decode": dec,
+        "decode_paged": dec_paged,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -149,6 +149,49 @@ qwen3_attn_status qwen3_attn_forward_prefill_chunk(qwen3_attn_t* h, const void* 
                                                    void* workspace, size_t workspace_bytes,
                                                    void* stream);
 
+/* Paged KV cache.  The pages name a preallocated pool of paged memory, read
+ * directly by the attention kernels, as what real serving systems use in
+ * place of a cache grown with torch.cat ("Assembling a large model from
+ * scratch": the self-test's fifth answer, the notes after "The complete
+ * code", and "Inference view").  They fix no layout; the one here:
+ *   k_pool, v_pool [num_blocks, n_kv, block_size, d_head], dtype of the block;
+ *   block_table    [B or N, max_blocks] int32 DEVICE array: the keys/values of
+ *                  token position p of sequence b live in physical block
+ *                  block_table[b * max_blocks + p / block_size], row
+ *                  p % block_size.
+ * block_size must be a power of two >= 64 (EINVAL otherwise); max_blocks > 0.
+ * Device preconditions (not checked): every table entry a sequence uses
+ * indexes a block of the pools, and no two sequences write the same block.
+ *
+ * Chunked prefill over a paged cache: as qwen3_attn_forward_prefill_chunk
+ * with slot p of sequence b at the block the table gives.  past_len may be
+ * NULL (empty caches).  Precondition: past_len[b] + T <= max_blocks *
+ * block_size.  Workspace: qwen3_attn_workspace_size(desc, 0, B, T, 0). */
+qwen3_attn_status qwen3_attn_forward_prefill_paged(qwen3_attn_t* h, const void* hidden,
+                                                   const int32_t* positions,
+                                                   const int32_t* past_len,
+                                                   const int32_t* block_table,
+                                                   int32_t max_blocks,
+                                                   void* k_pool, void* v_pool,
+                                                   int32_t block_size, void* out,
+                                                   int32_t B, int32_t T,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   void* stream);
+
+/* Decode over a paged cache: as qwen3_attn_forward_decode (positions[s] =
+ * L_s cached tokens; the new token is written at position L_s and attends to
+ * positions 0..L_s), with the rows found through the block table.
+ * Precondition: L_s < max_blocks * block_size.  Workspace:
+ * qwen3_attn_workspace_size(desc, 1, N, 1, max_blocks * block_size). */
+qwen3_attn_status qwen3_attn_forward_decode_paged(qwen3_attn_t* h, const void* hidden,
+                                                  const int32_t* positions,
+                                                  const int32_t* block_table,
+                                                  int32_t max_blocks,
+                                                  void* k_pool, void* v_pool,
+                                                  int32_t block_size, void* out, int32_t N,
+                                                  void* workspace, size_t workspace_bytes,
+                                                  void* stream);
+
 /* Decode: one new token for each of N sequences.
  *   hidden    [N, d_model]
  *   positions [N] int32 device array, positions[s] = L_s = the number of

@@ -20,7 +20,8 @@ QWEN3_ATTN_F32 = 0
 QWEN3_ATTN_BF16 = 1
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EWORKSPACE", 5: "EHIP"}
 EXPORTED = ("qwen3_attn_create", "qwen3_attn_workspace_size", "qwen3_attn_forward_prefill",
-            "qwen3_attn_forward_prefill_chunk", "qwen3_attn_forward_decode", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
+            "qwen3_attn_forward_prefill_chunk", "qwen3_attn_forward_prefill_paged",
+            "qwen3_attn_forward_decode", "qwen3_attn_forward_decode_paged", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
             "qwen3_attn_stage_times", "qwen3_attn_status_string")
 STAGES = ("qkv_norm_rope_gemm", "attention", "o_proj_gemm")
 
@@ -64,6 +65,12 @@ def lib() -> ctypes.CDLL:
         L.qwen3_attn_forward_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i32, i32,
                                                        vp, sz, vp]
         L.qwen3_attn_forward_prefill_chunk.restype = ctypes.c_int
+        L.qwen3_attn_forward_prefill_paged.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, i32,
+                                                       i32, vp, sz, vp]
+        L.qwen3_attn_forward_prefill_paged.restype = ctypes.c_int
+        L.qwen3_attn_forward_decode_paged.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, vp, i32, vp,
+                                                      sz, vp]
+        L.qwen3_attn_forward_decode_paged.restype = ctypes.c_int
         L.qwen3_attn_forward_decode.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, vp]
         L.qwen3_attn_forward_decode.restype = ctypes.c_int
         L.qwen3_attn_destroy.argtypes = [vp]
@@ -108,6 +115,22 @@ def qwen3_attn_forward_prefill_chunk(handle, hidden, positions, past_len, k_cach
     return lib().qwen3_attn_forward_prefill_chunk(handle, hidden, positions, past_len, k_cache,
                                                   v_cache, cache_cap, out, B, T, workspace,
                                                   workspace_bytes, stream)
+
+
+def qwen3_attn_forward_prefill_paged(handle, hidden, positions, past_len, block_table, max_blocks,
+                                     k_pool, v_pool, block_size, out, B, T, workspace,
+                                     workspace_bytes, stream) -> int:
+    return lib().qwen3_attn_forward_prefill_paged(handle, hidden, positions, past_len, block_table,
+                                                  max_blocks, k_pool, v_pool, block_size, out, B, T,
+                                                  workspace, workspace_bytes, stream)
+
+
+def qwen3_attn_forward_decode_paged(handle, hidden, positions, block_table, max_blocks, k_pool,
+                                    v_pool, block_size, out, N, workspace, workspace_bytes,
+                                    stream) -> int:
+    return lib().qwen3_attn_forward_decode_paged(handle, hidden, positions, block_table, max_blocks,
+                                                 k_pool, v_pool, block_size, out, N, workspace,
+                                                 workspace_bytes, stream)
 
 
 def qwen3_attn_forward_decode(handle, hidden, positions, k_cache, v_cache, cache_cap, out, N,
@@ -255,6 +278,50 @@ class Qwen3Attention:
             torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise Qwen3AttnError("qwen3_attn_forward_prefill_chunk", st)
+        return out
+
+    def prefill_paged(self, hidden, positions, past_len, block_table, k_pool, v_pool, out=None,
+                      workspace=None):
+        """Chunked prefill over a paged cache: pools [num_blocks, n_kv, block_size, 128];
+        block_table [B, max_blocks] int32 (device); past_len [B] int32 (device) or None."""
+        torch = _torch()
+        B, T, d = hidden.shape
+        nb, _, bs, _ = k_pool.shape
+        mb = block_table.shape[1]
+        if out is None:
+            out = torch.empty_like(hidden)
+        ws = self._workspace(self.workspace_size(False, B, T), workspace)
+        st = qwen3_attn_forward_prefill_paged(
+            self.handle, _ptr(hidden, "hidden", self.dtype), _ptr(positions, "positions", torch.int32, (B, T)),
+            None if past_len is None else _ptr(past_len, "past_len", torch.int32, (B,)),
+            _ptr(block_table, "block_table", torch.int32, (B, mb)), mb,
+            _ptr(k_pool, "k_pool", self.dtype, (nb, self.n_kv, bs, self.d_head)),
+            _ptr(v_pool, "v_pool", self.dtype, (nb, self.n_kv, bs, self.d_head)), bs,
+            _ptr(out, "out", self.dtype, (B, T, d)), B, T, _ptr(ws, "workspace"),
+            ws.numel() * ws.element_size(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise Qwen3AttnError("qwen3_attn_forward_prefill_paged", st)
+        return out
+
+    def decode_paged(self, hidden, positions, block_table, k_pool, v_pool, out=None,
+                     workspace=None):
+        """Decode over a paged cache; positions [N] int32 = cached lengths."""
+        torch = _torch()
+        N, d = hidden.shape
+        nb, _, bs, _ = k_pool.shape
+        mb = block_table.shape[1]
+        if out is None:
+            out = torch.empty_like(hidden)
+        ws = self._workspace(self.workspace_size(True, N, 1, mb * bs), workspace)
+        st = qwen3_attn_forward_decode_paged(
+            self.handle, _ptr(hidden, "hidden", self.dtype), _ptr(positions, "positions", torch.int32, (N,)),
+            _ptr(block_table, "block_table", torch.int32, (N, mb)), mb,
+            _ptr(k_pool, "k_pool", self.dtype, (nb, self.n_kv, bs, self.d_head)),
+            _ptr(v_pool, "v_pool", self.dtype, (nb, self.n_kv, bs, self.d_head)), bs,
+            _ptr(out, "out", self.dtype, (N, d)), N, _ptr(ws, "workspace"),
+            ws.numel() * ws.element_size(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise Qwen3AttnError("qwen3_attn_forward_decode_paged", st)
         return out
 
     def decode(self, hidden, positions, k_cache, v_cache, out=None, workspace=None):

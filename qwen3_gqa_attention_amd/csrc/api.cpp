@@ -130,9 +130,9 @@ qwen3_attn_status hip_status(hipError_t e) {
 
 template <typename T>
 qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
-                              const int32_t* past, void* k_cache, void* v_cache, int64_t cap,
-                              void* out, int B, int T_len, char* ws, const WsLayout& L,
-                              hipStream_t s) {
+                              const int32_t* past, void* k_cache, void* v_cache,
+                              const q3::KvAddr& kv, void* out, int B, int T_len, char* ws,
+                              const WsLayout& L, hipStream_t s) {
   const qwen3_attn_desc& d = h->desc;
   const int M = B * T_len;
   const int nqkv = (d.n_q + 2 * d.n_kv) * 128;
@@ -141,7 +141,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
-                    d.n_q, d.n_kv, cap, T_len, 0, d.eps, past, q3::kScoreScaleLog2};
+                    d.n_q, d.n_kv, kv, T_len, 0, d.eps, past, q3::kScoreScaleLog2};
   mark(h, s, 0);
   hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, M, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
@@ -152,7 +152,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   mark(h, s, 1);
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                   reinterpret_cast<const T*>(v_cache), abuf, B, T_len, d.n_q, d.n_kv,
-                                  cap, past, reinterpret_cast<float*>(ws + L.part_off), s);
+                                  kv, past, reinterpret_cast<float*>(ws + L.part_off), s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
@@ -163,8 +163,8 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
 
 template <typename T>
 qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
-                             void* k_cache, void* v_cache, int64_t cap, void* out, int N, char* ws,
-                             const WsLayout& L, hipStream_t s) {
+                             void* k_cache, void* v_cache, const q3::KvAddr& kv, void* out, int N,
+                             char* ws, const WsLayout& L, hipStream_t s) {
   const qwen3_attn_desc& d = h->desc;
   const int nqkv = (d.n_q + 2 * d.n_kv) * 128;
   const int hq = d.n_q * 128;
@@ -172,7 +172,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
-                    d.n_q, d.n_kv, cap, 1, 1, d.eps, nullptr, q3::kScoreScaleLog2};
+                    d.n_q, d.n_kv, kv, 1, 1, d.eps, nullptr, q3::kScoreScaleLog2};
   mark(h, s, 0);
   float* part = L.part ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
   hipError_t r = hipSuccess;
@@ -190,7 +190,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   mark(h, s, 1);
   r = q3::launch_decode_attn<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                 reinterpret_cast<const T*>(v_cache), positions, abuf, N, d.n_q,
-                                d.n_kv, cap, sc, s);
+                                d.n_kv, kv, sc, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
@@ -279,13 +279,28 @@ size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
 }
 
 namespace {
+// Paged cache addressing from the caller's block size (0 if unsupported).
+bool paged_addr(const qwen3_attn_desc& d, const int32_t* table, int32_t max_blocks,
+                int32_t block_size, q3::KvAddr* kv) {
+  if (!table || max_blocks <= 0 || block_size < 64 || block_size > (1 << 20) ||
+      (block_size & (block_size - 1)) != 0)
+    return false;
+  if ((int64_t)max_blocks * block_size > INT_MAX) return false;
+  int lg = 0;
+  while ((1 << lg) < block_size) ++lg;
+  *kv = q3::KvAddr{table, block_size, max_blocks, lg, d.n_kv};
+  return true;
+}
+
 qwen3_attn_status prefill_entry(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
                                 const int32_t* past, void* k_cache, void* v_cache,
-                                int64_t cache_cap, void* out, int32_t B, int32_t T,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                const q3::KvAddr* paged, int64_t cache_cap, void* out, int32_t B,
+                                int32_t T, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   if (!h || !hidden || !positions || !k_cache || !v_cache || !out) return QWEN3_ATTN_EINVAL;
   if (B <= 0 || T <= 0 || cache_cap <= 0 || T > cache_cap) return QWEN3_ATTN_EINVAL;
   if (B > 65535 || cache_cap > INT_MAX) return QWEN3_ATTN_EUNSUPPORTED;
+  const q3::KvAddr kv = paged ? *paged : q3::KvAddr{nullptr, cache_cap, 0, 0, h->desc.n_kv};
   WsLayout L;
   if (!ws_layout(&h->desc, 0, B, T, cache_cap, &L)) return QWEN3_ATTN_EUNSUPPORTED;
   if (!workspace || workspace_bytes < L.total) return QWEN3_ATTN_EWORKSPACE;
@@ -294,38 +309,16 @@ qwen3_attn_status prefill_entry(qwen3_attn_t* h, const void* hidden, const int32
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (h->desc.dtype == QWEN3_ATTN_F32)
-    return run_prefill<float>(h, hidden, positions, past, k_cache, v_cache, cache_cap, out, B, T,
-                              ws, L, s);
-  return run_prefill<q3::bf16_t>(h, hidden, positions, past, k_cache, v_cache, cache_cap, out, B,
-                                 T, ws, L, s);
-}
-}  // namespace
-
-qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,
-                                             const int32_t* positions, void* k_cache,
-                                             void* v_cache, int64_t cache_cap, void* out,
-                                             int32_t B, int32_t T, void* workspace,
-                                             size_t workspace_bytes, void* stream) {
-  return prefill_entry(h, hidden, positions, nullptr, k_cache, v_cache, cache_cap, out, B, T,
-                       workspace, workspace_bytes, stream);
+    return run_prefill<float>(h, hidden, positions, past, k_cache, v_cache, kv, out, B, T, ws, L,
+                              s);
+  return run_prefill<q3::bf16_t>(h, hidden, positions, past, k_cache, v_cache, kv, out, B, T, ws,
+                                 L, s);
 }
 
-qwen3_attn_status qwen3_attn_forward_prefill_chunk(qwen3_attn_t* h, const void* hidden,
-                                                   const int32_t* positions,
-                                                   const int32_t* past_len, void* k_cache,
-                                                   void* v_cache, int64_t cache_cap, void* out,
-                                                   int32_t B, int32_t T, void* workspace,
-                                                   size_t workspace_bytes, void* stream) {
-  if (!past_len) return QWEN3_ATTN_EINVAL;
-  return prefill_entry(h, hidden, positions, past_len, k_cache, v_cache, cache_cap, out, B, T,
-                       workspace, workspace_bytes, stream);
-}
-
-qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,
-                                            const int32_t* positions, void* k_cache,
-                                            void* v_cache, int64_t cache_cap, void* out,
-                                            int32_t N, void* workspace, size_t workspace_bytes,
-                                            void* stream) {
+qwen3_attn_status decode_entry(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
+                               void* k_cache, void* v_cache, const q3::KvAddr* paged,
+                               int64_t cache_cap, void* out, int32_t N, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (!h || !hidden || !positions || !k_cache || !v_cache || !out) return QWEN3_ATTN_EINVAL;
   if (N <= 0 || cache_cap <= 0) return QWEN3_ATTN_EINVAL;
   if (N > 65535 || cache_cap > INT_MAX) return QWEN3_ATTN_EUNSUPPORTED;
@@ -335,12 +328,71 @@ qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,
   if (!workspace || workspace_bytes < L.total) return QWEN3_ATTN_EWORKSPACE;
   qwen3_attn_status st = check_handle_device(h);
   if (st != QWEN3_ATTN_OK) return st;
+  const q3::KvAddr kv = paged ? *paged : q3::KvAddr{nullptr, cache_cap, 0, 0, h->desc.n_kv};
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (h->desc.dtype == QWEN3_ATTN_F32)
-    return run_decode<float>(h, hidden, positions, k_cache, v_cache, cache_cap, out, N, ws, L, s);
-  return run_decode<q3::bf16_t>(h, hidden, positions, k_cache, v_cache, cache_cap, out, N, ws, L,
-                                s);
+    return run_decode<float>(h, hidden, positions, k_cache, v_cache, kv, out, N, ws, L, s);
+  return run_decode<q3::bf16_t>(h, hidden, positions, k_cache, v_cache, kv, out, N, ws, L, s);
+}
+}  // namespace
+
+qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,
+                                             const int32_t* positions, void* k_cache,
+                                             void* v_cache, int64_t cache_cap, void* out,
+                                             int32_t B, int32_t T, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return prefill_entry(h, hidden, positions, nullptr, k_cache, v_cache, nullptr, cache_cap, out,
+                       B, T, workspace, workspace_bytes, stream);
+}
+
+qwen3_attn_status qwen3_attn_forward_prefill_chunk(qwen3_attn_t* h, const void* hidden,
+                                                   const int32_t* positions,
+                                                   const int32_t* past_len, void* k_cache,
+                                                   void* v_cache, int64_t cache_cap, void* out,
+                                                   int32_t B, int32_t T, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  if (!past_len) return QWEN3_ATTN_EINVAL;
+  return prefill_entry(h, hidden, positions, past_len, k_cache, v_cache, nullptr, cache_cap, out,
+                       B, T, workspace, workspace_bytes, stream);
+}
+
+qwen3_attn_status qwen3_attn_forward_prefill_paged(qwen3_attn_t* h, const void* hidden,
+                                                   const int32_t* positions,
+                                                   const int32_t* past_len,
+                                                   const int32_t* block_table,
+                                                   int32_t max_blocks, void* k_pool, void* v_pool,
+                                                   int32_t block_size, void* out, int32_t B,
+                                                   int32_t T, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  if (!h) return QWEN3_ATTN_EINVAL;
+  q3::KvAddr kv;
+  if (!paged_addr(h->desc, block_table, max_blocks, block_size, &kv)) return QWEN3_ATTN_EINVAL;
+  return prefill_entry(h, hidden, positions, past_len, k_pool, v_pool, &kv,
+                       (int64_t)max_blocks * block_size, out, B, T, workspace, workspace_bytes,
+                       stream);
+}
+
+qwen3_attn_status qwen3_attn_forward_decode_paged(qwen3_attn_t* h, const void* hidden,
+                                                  const int32_t* positions,
+                                                  const int32_t* block_table, int32_t max_blocks,
+                                                  void* k_pool, void* v_pool, int32_t block_size,
+                                                  void* out, int32_t N, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
+  if (!h) return QWEN3_ATTN_EINVAL;
+  q3::KvAddr kv;
+  if (!paged_addr(h->desc, block_table, max_blocks, block_size, &kv)) return QWEN3_ATTN_EINVAL;
+  return decode_entry(h, hidden, positions, k_pool, v_pool, &kv, (int64_t)max_blocks * block_size,
+                      out, N, workspace, workspace_bytes, stream);
+}
+
+qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,
+                                            const int32_t* positions, void* k_cache,
+                                            void* v_cache, int64_t cache_cap, void* out,
+                                            int32_t N, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  return decode_entry(h, hidden, positions, k_cache, v_cache, nullptr, cache_cap, out, N,
+                      workspace, workspace_bytes, stream);
 }
 
 void qwen3_attn_destroy(qwen3_attn_t* h) {

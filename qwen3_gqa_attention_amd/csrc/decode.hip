@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
                                                           const int32_t* __restrict__ positions,
                                                           float* __restrict__ part_acc,
                                                           float* __restrict__ part_ml, int n_q,
-                                                          int n_kv, int64_t cap, int nchunk) {
+                                                          int n_kv, KvAddr kv, int nchunk) {
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int nkeys = positions[s] + 1;
   const int k0 = c * kDecodeChunk;
@@ -99,10 +99,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
   }
 
-  const T* Kg = Kc + (size_t)(s * n_kv + g) * cap * kHeadDim + oct * 8;
-  const T* Vg = Vc + (size_t)(s * n_kv + g) * cap * kHeadDim + oct * 8;
+  const T* Kl = Kc + oct * 8;
+  const T* Vl = Vc + oct * 8;
   constexpr int U = kDecodeUnroll;
   for (int kb = wk0; kb < wk1; kb += 4 * U) {
+    // The 4U keys from kb (a multiple of 4U) lie in one cache block.
+    const int64_t r0 = kv.row(s, g, kb);
     RowSlice<T> kr[U], vr[U];
     bool val[U];
 #pragma unroll
@@ -110,8 +112,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
       const int key = kb + grp + 4 * u;
       val[u] = key < wk1;
       if (val[u]) {
-        kr[u].load_stream(Kg + (size_t)key * kHeadDim);
-        vr[u].load_stream(Vg + (size_t)key * kHeadDim);
+        kr[u].load_stream(Kl + (r0 + grp + 4 * u) * kHeadDim);
+        vr[u].load_stream(Vl + (r0 + grp + 4 * u) * kHeadDim);
       } else {
         kr[u].zero();
         vr[u].zero();
@@ -242,25 +244,25 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
 
 template <typename T, int NREP>
 static void launch_decode_nrep(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
-                               int N, int n_q, int n_kv, int64_t cap, const DecodeScratch& ws,
+                               int N, int n_q, int n_kv, const KvAddr& kv, const DecodeScratch& ws,
                                hipStream_t s) {
   hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(ws.nchunk, n_kv, N), dim3(256), 0, s, Q,
-                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, cap, ws.nchunk);
+                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, kv, ws.nchunk);
 }
 
 template <typename T>
 hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
-                              T* Out, int N, int n_q, int n_kv, int64_t cap,
+                              T* Out, int N, int n_q, int n_kv, const KvAddr& kv,
                               const DecodeScratch& ws, hipStream_t s) {
   switch (n_q / n_kv) {
-    case 1: launch_decode_nrep<T, 1>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
-    case 2: launch_decode_nrep<T, 2>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
-    case 3: launch_decode_nrep<T, 3>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
-    case 4: launch_decode_nrep<T, 4>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
-    case 5: launch_decode_nrep<T, 5>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
-    case 6: launch_decode_nrep<T, 6>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
-    case 8: launch_decode_nrep<T, 8>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
-    case 16: launch_decode_nrep<T, 16>(Q, Kc, Vc, positions, N, n_q, n_kv, cap, ws, s); break;
+    case 1: launch_decode_nrep<T, 1>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
+    case 2: launch_decode_nrep<T, 2>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
+    case 3: launch_decode_nrep<T, 3>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
+    case 4: launch_decode_nrep<T, 4>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
+    case 5: launch_decode_nrep<T, 5>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
+    case 6: launch_decode_nrep<T, 6>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
+    case 8: launch_decode_nrep<T, 8>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
+    case 16: launch_decode_nrep<T, 16>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -276,10 +278,10 @@ bool decode_nrep_supported(int n_rep) {
 }
 
 template hipError_t launch_decode_attn<float>(const float*, const float*, const float*,
-                                              const int32_t*, float*, int, int, int, int64_t,
+                                              const int32_t*, float*, int, int, int, const KvAddr&,
                                               const DecodeScratch&, hipStream_t);
 template hipError_t launch_decode_attn<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
-                                               const int32_t*, bf16_t*, int, int, int, int64_t,
+                                               const int32_t*, bf16_t*, int, int, int, const KvAddr&,
                                                const DecodeScratch&, hipStream_t);
 
 }  // namespace q3

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc,
                                                             T* __restrict__ Out, int B, int T_len,
-                                                            int n_q, int n_kv, int64_t cap,
+                                                            int n_q, int n_kv, KvAddr kv,
                                                             const int32_t* __restrict__ past,
                                                             int nsplit,
                                                             float* __restrict__ part) {
@@ -137,8 +137,9 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     for (int ks = 0; ks < DSTEPS; ++ks) qf[ks] = row_ok ? MF::load(qrow + ks * MF::K) : MF::zero();
   }
 
-  const T* Kg = Kc + (size_t)(b * n_kv + g) * cap * kHeadDim;
-  const T* Vg = Vc + (size_t)(b * n_kv + g) * cap * kHeadDim;
+  // Each key tile lies inside one cache block (paged block sizes are powers
+  // of two >= 64), so one row lookup per tile addresses all its rows.
+  auto tile_row = [&](int kbase) { return kv.row(b, g, kbase); };
 
   // ---- bf16 staging: direct global -> LDS loads -------------------------
   // One wave instruction (global_load_lds_dwordx4) fills 1 KB = 4 rows of
@@ -164,11 +165,12 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     const uint32_t lk = smem_lds + (uint32_t)((Ks(buf) - smem) * sizeof(T));
     const uint32_t lv = smem_lds + (uint32_t)((Vs(buf) - smem) * sizeof(T));
     const bool full = kbase + BN <= S_len;  // uniform
+    const int64_t r0 = tile_row(kbase);
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int key = full ? kbase + dma_row[j] : min(kbase + dma_row[j], S_len - 1);
-      const T* krow = Kg + (size_t)key * kHeadDim;
-      const T* vrow = Vg + (size_t)key * kHeadDim;
+      const int r = full ? dma_row[j] : min(kbase + dma_row[j], S_len - 1) - kbase;
+      const T* krow = Kc + (r0 + r) * kHeadDim;
+      const T* vrow = Vc + (r0 + r) * kHeadDim;
       const uint32_t r4b = (uint32_t)((j * 4 + hw) * 4 * LDK * sizeof(T));  // this instruction's first row
       dma16_to_lds(krow + dk_ch[j], lk + r4b);
       dma16_to_lds(vrow + dv_ch[j], lv + r4b);
@@ -180,13 +182,14 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   u32x4_v rkA[RCH], rvA[RCH];
   auto gload = [&](int kt) {
     const int kbase = kt * BN;
+    const int64_t r0 = tile_row(kbase);
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       const int c = th + i * 256, key = c >> 5, cc = c & 31;
-      const size_t off = (size_t)(kbase + key) * kHeadDim + cc * EPC;
+      const int64_t off = (r0 + key) * kHeadDim + cc * EPC;
       const bool ok = kbase + key < S_len;
-      rkA[i] = ok ? ld16(Kg + off) : u32x4_v{0u, 0u, 0u, 0u};
-      rvA[i] = ok ? ld16(Vg + off) : u32x4_v{0u, 0u, 0u, 0u};
+      rkA[i] = ok ? ld16(Kc + off) : u32x4_v{0u, 0u, 0u, 0u};
+      rvA[i] = ok ? ld16(Vc + off) : u32x4_v{0u, 0u, 0u, 0u};
     }
   };
   auto sstore = [&](int buf) {
@@ -522,7 +525,8 @@ size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv) {
 
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
-                                int n_q, int n_kv, int64_t cap, const int32_t* past, float* part,
+                                int n_q, int n_kv, const KvAddr& kv, const int32_t* past,
+                                float* part,
                                 hipStream_t s) {
   const int nsplit = flash_splits(B, T_len, n_q, n_kv);
   if (nsplit > 1 && !part) return hipErrorInvalidValue;
@@ -532,10 +536,10 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
   const int wgs = flash_query_wgs(B, T_len, n_q, n_kv) * nsplit;
   if (wgs < 4 * 256)
     hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, cap, past, nsplit, part);
+                       T_len, n_q, n_kv, kv, past, nsplit, part);
   else
     hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, cap, past, nsplit, part);
+                       T_len, n_q, n_kv, kv, past, nsplit, part);
   if (nsplit > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -547,10 +551,10 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
 }
 
 template hipError_t launch_flash_prefill<float>(const float*, const float*, const float*, float*,
-                                                int, int, int, int, int64_t, const int32_t*,
-                                                float*, hipStream_t);
+                                                int, int, int, int, const KvAddr&,
+                                                const int32_t*, float*, hipStream_t);
 template hipError_t launch_flash_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
-                                                 bf16_t*, int, int, int, int, int64_t,
+                                                 bf16_t*, int, int, int, int, const KvAddr&,
                                                  const int32_t*, float*, hipStream_t);
 
 }  // namespace q3

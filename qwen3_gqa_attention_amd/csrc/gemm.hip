@@ -317,7 +317,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
       const int slot = qe.decode ? qe.positions[row]
                                  : row % qe.rows_per_seq + (qe.past ? qe.past[seq] : 0);
       T* cache = reinterpret_cast<T*>(kind == 1 ? qe.k_cache : qe.v_cache);
-      return cache + ((size_t)(seq * qe.n_kv + g) * qe.cap + slot) * kHeadDim;
+      return cache + qe.kv.row(seq, g, slot) * kHeadDim;
     }
   };
 
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
     const int slot = qe.decode ? qe.positions[row]
                                : row % qe.rows_per_seq + (qe.past ? qe.past[seq] : 0);
     T* cache = reinterpret_cast<T*>(kind == 1 ? qe.k_cache : qe.v_cache);
-    dst = cache + ((size_t)(seq * qe.n_kv + g) * qe.cap + slot) * kHeadDim;
+    dst = cache + qe.kv.row(seq, g, slot) * kHeadDim;
   }
   dst += j * 8;
 #pragma unroll

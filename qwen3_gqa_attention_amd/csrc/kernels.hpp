@@ -14,6 +14,26 @@ typedef uint16_t bf16_t;
 // q' = q * kScoreScaleLog2, so the attention kernels use the hardware exp2.
 constexpr float kScoreScaleLog2 = 0.1275174308f;
 
+// Where the cached key/value row of (sequence, KV head, key position) lives.
+//   contiguous (table == nullptr): caches [seqs, n_kv, cap, 128];
+//   paged: pools [num_blocks, n_kv, block_size, 128] and an int32 block table
+//   [seqs, max_blocks]: logical block key / block_size of sequence seq is
+//   physical block table[seq * max_blocks + key / block_size].
+// block_size is a power of two >= 64, so a 64-key tile never straddles a
+// block.  row() is the row index in units of 128 elements.
+struct KvAddr {
+  const int32_t* table;
+  int64_t cap;     // contiguous: slots per (sequence, head); paged: block_size
+  int max_blocks;  // paged: block-table row length
+  int log2_bs;     // paged: log2(block_size)
+  int n_kv;
+  __host__ __device__ __forceinline__ int64_t row(int seq, int g, int key) const {
+    if (!table) return ((int64_t)seq * n_kv + g) * cap + key;
+    const int64_t blk = table[(int64_t)seq * max_blocks + (key >> log2_bs)];
+    return ((blk * n_kv + g) << log2_bs) + (key & ((1 << log2_bs) - 1));
+  }
+};
+
 struct QkvEpilogue {
   void* q_out;               // [rows, n_q*128]
   void* k_cache;             // [seqs, n_kv, cap, 128]
@@ -23,7 +43,7 @@ struct QkvEpilogue {
   const void* gk;            // [128] k_norm gain
   const float2* rope_cs;     // [rows][64] (cos, sin) of position * omega_i
   int n_q, n_kv;
-  int64_t cap;
+  KvAddr kv;                 // cache addressing (contiguous or paged)
   int rows_per_seq;          // prefill: T (slot = past + row % T); decode: 1
   int decode;                // 1: cache slot = positions[row]
   float eps;
@@ -63,8 +83,8 @@ int small_m_partial_floats(int M, int N, int K, int elem_size);
 // workgroups and merged by a second kernel.
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
-                                int n_q, int n_kv, int64_t cap, const int32_t* past, float* part,
-                                hipStream_t s);
+                                int n_q, int n_kv, const KvAddr& kv, const int32_t* past,
+                                float* part, hipStream_t s);
 int flash_splits(int B, int T_len, int n_q, int n_kv);
 size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv);
 
@@ -80,7 +100,7 @@ int decode_chunk_keys();
 bool decode_nrep_supported(int n_rep);
 template <typename T>
 hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
-                              T* Out, int N, int n_q, int n_kv, int64_t cap,
+                              T* Out, int N, int n_q, int n_kv, const KvAddr& kv,
                               const DecodeScratch& ws, hipStream_t s);
 
 }  // namespace q3

@@ -105,6 +105,10 @@ def test_forward_with_null_handle_is_einval(built_lib):
                                                None) == 1
     assert q3.qwen3_attn_forward_prefill_chunk(None, 1, 1, 1, 1, 1, 16, 1, 1, 8, 1, 1 << 20,
                                                None) == 1
+    assert q3.qwen3_attn_forward_prefill_paged(None, 1, 1, None, 1, 4, 1, 1, 64, 1, 1, 8, 1,
+                                               1 << 20, None) == 1
+    assert q3.qwen3_attn_forward_decode_paged(None, 1, 1, 1, 4, 1, 1, 64, 1, 1, 1, 1 << 20,
+                                              None) == 1
     assert q3.qwen3_attn_forward_decode(None, 1, 1, 1, 1, 16, 1, 1, 1, 1 << 20, None) == 1
     q3.qwen3_attn_destroy(None)   # NULL is a no-op
 

@@ -355,6 +355,162 @@ def test_decode_full_size_sampled_sequences():
     torch.cuda.empty_cache()
 
 
+# --------------------------------------------------------------------- paged KV
+def to_paged(kc, vc, lengths, bs, *, seed=0, spare=3):
+    """Scatter contiguous host caches [S, n_kv, cap, dh] into pools
+    [num_blocks, n_kv, bs, dh] under a random block table covering lengths[s]
+    (+ the slots the call writes); unused blocks hold NaN."""
+    S, n_kv, cap, dh = kc.shape
+    need = [(int(L) + bs - 1) // bs for L in lengths]
+    mb = max(max(need), 1)
+    nb = sum(need) + spare
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(nb)
+    table = np.zeros((S, mb), np.int32)
+    kp = np.full((nb, n_kv, bs, dh), np.nan, np.float32)
+    vp = np.full_like(kp, np.nan)
+    nxt = 0
+    for s in range(S):
+        for i in range(need[s]):
+            blk = int(perm[nxt]); nxt += 1
+            table[s, i] = blk
+            lo, hi = i * bs, min((i + 1) * bs, cap)
+            kp[blk, :, : hi - lo] = kc[s, :, lo:hi]
+            vp[blk, :, : hi - lo] = vc[s, :, lo:hi]
+        table[s, need[s]:] = table[s, max(need[s] - 1, 0)]   # never reached
+    return kp, vp, table
+
+
+def from_paged(pool, table, s, L):
+    bs = pool.shape[2]
+    rows = [pool[table[s, p // bs], :, p % bs] for p in range(L)]
+    return np.stack(rows, axis=1) if rows else np.zeros((pool.shape[1], 0, pool.shape[3]))
+
+
+@pytest.mark.parametrize("dtype,bs", [("bf16", 64), ("bf16", 256), ("f32", 128)])
+def test_decode_paged_parity(dtype, bs):
+    import torch
+    w = dataclasses.replace(WORKLOADS[5], dtype=dtype)
+    say(f"paged decode parity: dtype={dtype} block_size={bs}")
+    lens = np.array([0, 1, 63, 64, 65, 511, 1030, 2047], np.int32)
+    inp = decode_inputs(w, N=len(lens))
+    inp["positions"] = lens
+    cap = 2112
+    kc, vc = decode_cache_host(w, lens, cap)
+    kp, vp, table = to_paged(kc, vc, lens + 1, bs, seed=bs)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    kpd, vpd = dev(kp, w.dtype), dev(vp, w.dtype)
+    y = blk.decode_paged(dev(inp["X"], w.dtype), torch.from_numpy(lens).to("cuda"),
+                         torch.from_numpy(table).to("cuda"), kpd, vpd)
+    torch.cuda.synchronize()
+    kp_got, vp_got = host(kpd), host(vpd)
+    ref = oracle.decode(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], inp["gq"], inp["gk"],
+                        lens, kc, vc, n_q=w.n_q, n_kv=w.n_kv, eps=EPS, theta=ROPE_THETA)
+    assert_close(host(y), ref["Y"], w.dtype, "paged decode Y")
+    for s, L in enumerate(lens):
+        k_all = from_paged(kp_got, table, s, int(L) + 1)
+        v_all = from_paged(vp_got, table, s, int(L) + 1)
+        np.testing.assert_array_equal(k_all[:, :L], kc[s, :, :L])
+        assert_close(k_all[:, L], ref["k_new"][s], w.dtype, f"new k seq {s}")
+        assert_close(v_all[:, L], ref["v_new"][s], w.dtype, f"new v seq {s}")
+    # the contiguous path gives the same result bit for bit
+    got_c = run_decode_gpu(w, inp, kc, vc, cap)
+    np.testing.assert_array_equal(host(y), got_c["Y"])
+    used = set(table[s, i] for s in range(len(lens)) for i in range((int(lens[s]) + bs) // bs))
+    for b in range(kp.shape[0]):
+        if b not in used:
+            assert np.all(np.isnan(kp_got[b])), "a block outside the tables was written"
+    blk.close()
+
+
+@pytest.mark.parametrize("dtype,bs,T,past", [("bf16", 64, 70, [0, 100, 300]),
+                                             ("bf16", 128, 150, [37, 1000]),
+                                             ("f32", 64, 58, [70])])
+def test_prefill_paged_parity(dtype, bs, T, past):
+    import torch
+    idx = 1 if dtype == "f32" else 2
+    w, inp, past, kc, vc = chunk_case(idx, len(past), T, past)
+    say(f"paged chunked prefill parity: {w.name} block_size={bs} T={T} past={past.tolist()}")
+    kp, vp, table = to_paged(kc, vc, past + T, bs, seed=T)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    kpd, vpd = dev(kp, w.dtype), dev(vp, w.dtype)
+    y = blk.prefill_paged(dev(inp["X"], w.dtype), torch.from_numpy(inp["positions"]).to("cuda"),
+                          torch.from_numpy(past).to("cuda"), torch.from_numpy(table).to("cuda"),
+                          kpd, vpd)
+    torch.cuda.synchronize()
+    ref = oracle_chunk(w, inp, past, kc, vc)
+    assert_close(host(y), ref["Y"], w.dtype, "paged chunked prefill Y")
+    kp_got, vp_got = host(kpd), host(vpd)
+    for b, P in enumerate(past):
+        k_all = from_paged(kp_got, table, b, int(P) + T)
+        v_all = from_paged(vp_got, table, b, int(P) + T)
+        np.testing.assert_array_equal(k_all[:, :P], kc[b, :, :P])
+        assert_close(k_all[:, P:], ref["Kc"][b], w.dtype, f"k chunk seq {b}")
+        assert_close(v_all[:, P:], ref["Vc"][b], w.dtype, f"v chunk seq {b}")
+    got_c = run_chunk_gpu(w, inp, past, kc, vc)
+    np.testing.assert_array_equal(host(y), got_c["Y"])
+    blk.close()
+
+
+def test_decode_paged_full_size_equals_contiguous():
+    # 64 sequences of 1024..32768 cached tokens in 64-token blocks laid out in
+    # a shuffled pool: the paged call equals the contiguous one bit for bit
+    # (the contiguous path is checked against the oracle at this size above).
+    import torch
+    w = WORKLOADS[5]
+    say(f"paged decode full size: {w.name}")
+    inp = decode_inputs(w)
+    L = inp["positions"]
+    bs = 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 3)
+    kc = torch.randn((w.B, w.n_kv, w.cap, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((w.B, w.n_kv, w.cap, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    mb = w.cap // bs
+    nb = w.B * mb
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(5)).to("cuda")
+    table = perm.view(w.B, mb).to(torch.int32).contiguous()
+    kp = torch.empty((nb, w.n_kv, bs, 128), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    # block (s, i) of the contiguous cache -> pool[table[s, i]]
+    kp[table.view(-1).long()] = kc.view(w.B, w.n_kv, mb, bs, 128).permute(0, 2, 1, 3, 4).reshape(nb, w.n_kv, bs, 128)
+    vp[table.view(-1).long()] = vc.view(w.B, w.n_kv, mb, bs, 128).permute(0, 2, 1, 3, 4).reshape(nb, w.n_kv, bs, 128)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(L).to("cuda")
+    y_p = blk.decode_paged(x, pos, table, kp, vp)
+    y_c = blk.decode(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(y_p), host(y_c))
+    blk.close()
+    del kc, vc, kp, vp
+    torch.cuda.empty_cache()
+
+
+def test_paged_argument_errors():
+    import torch
+    import qwen3_gqa_attention_amd as q3
+    w = WORKLOADS[2]
+    inp = prefill_inputs(w, B=1, T=8)
+    blk = block_from_inputs(inp, w.n_q, w.n_kv, w.dtype)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    pool = torch.zeros((4, w.n_kv, 64, 128), dtype=x.dtype, device="cuda")
+    table = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    ws = torch.empty(blk.workspace_size(False, 1, 8), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    P = lambda t: t.data_ptr()
+    f = q3.qwen3_attn_forward_prefill_paged
+    for bs in (32, 96, 0):   # not a power of two >= 64
+        assert f(blk.handle, P(x), P(pos), None, P(table), 4, P(pool), P(pool), bs, P(out), 1, 8,
+                 P(ws), ws.numel(), None) == 1
+    assert f(blk.handle, P(x), P(pos), None, None, 4, P(pool), P(pool), 64, P(out), 1, 8,
+             P(ws), ws.numel(), None) == 1                    # no block table
+    assert f(blk.handle, P(x), P(pos), None, P(table), 0, P(pool), P(pool), 64, P(out), 1, 8,
+             P(ws), ws.numel(), None) == 1                    # max_blocks 0
+    blk.close()
+
+
 def test_decode_equals_last_prefill_row_on_gpu():
     import torch
     w = WORKLOADS[2]
