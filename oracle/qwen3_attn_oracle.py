@@ -234,6 +234,29 @@ def prefill_chunk(x, wq, wk, wv, wo, gq, gk, positions, past_len, k_cache, v_cac
                 Vc=np.transpose(v, (0, 2, 1, 3)), A=A)
 
 
+def prefill_residual(x, g_in, wq, wk, wv, wo, gq, gk, positions, *, n_q, n_kv, dh=128,
+                     eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+    """The attention half of a decoder layer: x + block(RMSNorm(x) * g_in)
+    ([BUILD] "The complete code": input_layernorm, self-attention, residual
+    add).  Same arguments as prefill plus the input-norm gain g_in [d];
+    returns prefill's dict with Y replaced by the layer output."""
+    xd = np.asarray(x, dtype)
+    out = prefill(rms_norm(xd, g_in, eps), wq, wk, wv, wo, gq, gk, positions, n_q=n_q,
+                  n_kv=n_kv, dh=dh, eps=eps, theta=theta, dtype=dtype)
+    out["Y"] = xd + out["Y"]
+    return out
+
+
+def decode_residual(x, g_in, wq, wk, wv, wo, gq, gk, positions, k_cache, v_cache, *, n_q,
+                    n_kv, dh=128, eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+    """decode() with the input RMSNorm and the residual add around the block."""
+    xd = np.asarray(x, dtype)
+    out = decode(rms_norm(xd, g_in, eps), wq, wk, wv, wo, gq, gk, positions, k_cache, v_cache,
+                 n_q=n_q, n_kv=n_kv, dh=dh, eps=eps, theta=theta, dtype=dtype)
+    out["Y"] = xd + out["Y"]
+    return out
+
+
 def prefill_rows(x, wq, wk, wv, wo, gq, gk, positions, rows, *, n_q, n_kv, dh=128,
                  eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
     """The prefill output at selected tokens only, for full-size checks.

@@ -348,6 +348,57 @@ def test_chunked_prefill_ragged_past_and_special_cases():
     np.testing.assert_allclose(zero["Y"], run_prefill(p)["Y"], rtol=1e-12, atol=1e-13)
 
 
+def residual_args(p):
+    return {k: p[k] for k in ("x", "wq", "wk", "wv", "wo", "gq", "gk", "positions")}
+
+
+def test_layer_residual_is_identity_when_o_proj_is_zero():
+    # x + block(RMSNorm(x) g): with Wo = 0 the block adds nothing and the
+    # layer returns its input exactly (Assembling a large model, "The
+    # complete code": the residual add around the attention).
+    p = rand_block(31, B=2, T=7)
+    g_in = 1 + 0.1 * np.random.default_rng(1).standard_normal(p["x"].shape[-1])
+    a = residual_args(p)
+    a["wo"] = np.zeros_like(a["wo"])
+    out = oracle.prefill_residual(a.pop("x"), g_in, **a, n_q=p["n_q"], n_kv=p["n_kv"], dh=16)
+    np.testing.assert_array_equal(out["Y"], p["x"])
+
+
+def test_layer_block_sees_the_normalised_input():
+    # The block's input is RMS-normalised: scaling x by c > 0 scales the
+    # residual part only, so layer(c x) - c x = layer(x) - x (up to eps); and a
+    # row of the normalised input has RMS sqrt(m / (m + eps)) before the gain.
+    p = rand_block(32, B=1, T=6)
+    g_in = 1 + 0.1 * np.random.default_rng(2).standard_normal(p["x"].shape[-1])
+    a = residual_args(p)
+    x = a.pop("x")
+    base = oracle.prefill_residual(x, g_in, **a, n_q=p["n_q"], n_kv=p["n_kv"], dh=16)
+    big = oracle.prefill_residual(7.5 * x, g_in, **a, n_q=p["n_q"], n_kv=p["n_kv"], dh=16)
+    np.testing.assert_allclose(big["Y"] - 7.5 * x, base["Y"] - x, rtol=0, atol=1e-6)  # eps-level
+    xn = oracle.rms_norm(x, np.ones(x.shape[-1]), 1e-6)
+    m = np.mean(x ** 2, axis=-1)
+    np.testing.assert_allclose(np.sqrt(np.mean(xn ** 2, axis=-1)), np.sqrt(m / (m + 1e-6)),
+                               rtol=1e-13)
+    # without the norm and residual, the same weights give a different output
+    plain = oracle.prefill(x, **a, n_q=p["n_q"], n_kv=p["n_kv"], dh=16)
+    assert not np.allclose(base["Y"] - x, plain["Y"])
+
+
+def test_layer_decode_equals_last_layer_prefill_row():
+    p = rand_block(33, B=2, T=9)
+    g_in = 1 + 0.1 * np.random.default_rng(3).standard_normal(p["x"].shape[-1])
+    a = residual_args(p)
+    full = oracle.prefill_residual(a.pop("x"), g_in, **a, n_q=p["n_q"], n_kv=p["n_kv"], dh=16)
+    kc = np.zeros((2, p["n_kv"], 12, 16))
+    vc = np.zeros_like(kc)
+    kc[:, :, :8] = full["Kc"][:, :, :8]
+    vc[:, :, :8] = full["Vc"][:, :, :8]
+    dec = oracle.decode_residual(p["x"][:, 8], g_in, p["wq"], p["wk"], p["wv"], p["wo"], p["gq"],
+                                 p["gk"], np.array([8, 8]), kc, vc, n_q=p["n_q"], n_kv=p["n_kv"],
+                                 dh=16)
+    np.testing.assert_allclose(dec["Y"], full["Y"][:, 8], rtol=1e-12, atol=1e-13)
+
+
 def test_decode_ragged_lengths_and_empty_cache():
     # Sequences with different cache lengths, including 0, are independent.
     p = rand_block(16, B=3, T=6)
