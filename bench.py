@@ -141,7 +141,9 @@ def prefill_flops(B, T, d, n_q, n_kv, dh=128):
     }
 
 
-def bench_prefill(args):
+def bench_prefill(args, layer=False):
+    """The 0.6B-shaped prefill; with layer=True the block carries the fused
+    input RMSNorm and residual add (the attention half of a decoder layer)."""
     import numpy as np
     import torch
 
@@ -153,8 +155,12 @@ def bench_prefill(args):
     inp = prefill_inputs(w)
     bf = torch.bfloat16
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(bf)
+    g_in = None
+    if layer:
+        g_in = d(1 + 0.1 * np.random.default_rng(w.seed + 2).standard_normal(w.d))
     blk = q3.Qwen3Attention(d(inp["Wq"]), d(inp["Wk"]), d(inp["Wv"]), d(inp["Wo"]), d(inp["gq"]),
-                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA)
+                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA,
+                            input_norm=g_in)
     x = d(inp["X"])
     pos = torch.from_numpy(inp["positions"]).cuda()
     kc = torch.empty((B, w.n_kv, T, 128), dtype=bf, device="cuda")
@@ -407,8 +413,8 @@ def cpu_baseline(seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -443,6 +449,14 @@ def main():
     p = bench_prefill(args)
     log(f"bench: prefill {p['step_s'] * 1e3:.4f} ms/step; kernels " +
         ", ".join(f"{k} {v['avg_ms']:.4f} ms" for k, v in p["kernels"].items()))
+    log("bench: the same prefill with the fused input RMSNorm + residual add")
+    pl = bench_prefill(args, layer=True)
+    layer = {"workload": f"{pl['w'].name}-input-norm-residual",
+             "ms_per_step": pl["step_s"] * 1e3, "tokens_per_s": pl["B"] * pl["T"] / pl["step_s"],
+             "overhead_vs_block": pl["step_s"] / p["step_s"] - 1.0,
+             "kernel_ms": {k: v["avg_ms"] for k, v in pl["kernels"].items()}}
+    log(f"bench: layer prefill {layer['ms_per_step']:.4f} ms/step "
+        f"({layer['overhead_vs_block'] * 100:+.1f}% vs the block alone)")
     log("bench: chunked prefill 0.6B-shape B=2, 512 tokens over 1536 cached")
     chunk = bench_chunk(args)
     log(f"bench: chunked prefill {chunk['ms_per_step']:.4f} ms/step, "
@@ -504,6 +518,7 @@ def main():
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": p["flops"][dom] / (dk["avg_ms"] / 1e3) / PEAK_BF16_FLOPS,
                      "traffic": traffic.get("prefill_attention") if dom == "attention" else None},
+        "layer_prefill": layer,
         "chunked_prefill": chunk,
         "decode": dec,
         "decode_paged": dec_paged,

@@ -91,6 +91,24 @@ qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc,
                                     const qwen3_attn_weights* weights,
                                     void* stream, qwen3_attn_t** out);
 
+/* As qwen3_attn_create, for a handle that computes the attention half of a
+ * decoder layer: every forward call returns
+ *     out = hidden + block(RMSNorm(hidden) * input_norm)
+ * -- the pre-attention RMSNorm over d_model (eps inside the square root,
+ * eps from the descriptor) and the residual add around the block
+ * ("Assembling a large model from scratch", section "The complete code": the
+ * decoder layer's input_layernorm, attention and residual; "Qwen3
+ * Architecture Layer-by-Layer", section "Primitives - Qwen3RMSNorm").
+ *   input_norm [d_model] device array of the descriptor's dtype (copied into
+ *              the q/k/v weights: the gain is folded into their columns).
+ * The residual and the normalised input are both read from `hidden`; out
+ * must not overlap hidden.  EINVAL if input_norm is NULL, else as
+ * qwen3_attn_create. */
+qwen3_attn_status qwen3_attn_create_with_input_norm(const qwen3_attn_desc* desc,
+                                                    const qwen3_attn_weights* weights,
+                                                    const void* input_norm, void* stream,
+                                                    qwen3_attn_t** out);
+
 /* Bytes of workspace a forward call needs (0 if the arguments are invalid).
  * Pure host computation, no HIP call.
  *   is_decode = 0: prefill of B_or_N sequences of T tokens (cache_cap unused);

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libqwen3attn.so")
 QWEN3_ATTN_F32 = 0
 QWEN3_ATTN_BF16 = 1
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EWORKSPACE", 5: "EHIP"}
-EXPORTED = ("qwen3_attn_create", "qwen3_attn_workspace_size", "qwen3_attn_forward_prefill",
+EXPORTED = ("qwen3_attn_create", "qwen3_attn_create_with_input_norm", "qwen3_attn_workspace_size",
+            "qwen3_attn_forward_prefill",
             "qwen3_attn_forward_prefill_chunk", "qwen3_attn_forward_prefill_paged",
             "qwen3_attn_forward_decode", "qwen3_attn_forward_decode_paged", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
             "qwen3_attn_stage_times", "qwen3_attn_status_string")
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.qwen3_attn_create.argtypes = [ctypes.POINTER(Qwen3AttnDesc), ctypes.POINTER(Qwen3AttnWeights),
                                         vp, ctypes.POINTER(vp)]
         L.qwen3_attn_create.restype = ctypes.c_int
+        L.qwen3_attn_create_with_input_norm.argtypes = [ctypes.POINTER(Qwen3AttnDesc),
+                                                        ctypes.POINTER(Qwen3AttnWeights), vp, vp,
+                                                        ctypes.POINTER(vp)]
+        L.qwen3_attn_create_with_input_norm.restype = ctypes.c_int
         L.qwen3_attn_workspace_size.argtypes = [ctypes.POINTER(Qwen3AttnDesc), i32, i32, i32, i64]
         L.qwen3_attn_workspace_size.restype = sz
         L.qwen3_attn_forward_prefill.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, sz, vp]
@@ -95,6 +100,15 @@ def qwen3_attn_create(desc: Qwen3AttnDesc, weights: Qwen3AttnWeights, stream: in
     h = ctypes.c_void_p()
     st = lib().qwen3_attn_create(ctypes.byref(desc), ctypes.byref(weights), ctypes.c_void_p(stream),
                                  ctypes.byref(h))
+    return st, (h.value or 0)
+
+
+def qwen3_attn_create_with_input_norm(desc: Qwen3AttnDesc, weights: Qwen3AttnWeights, input_norm,
+                                      stream: int) -> tuple[int, int]:
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    st = lib().qwen3_attn_create_with_input_norm(ctypes.byref(desc), ctypes.byref(weights), input_norm,
+                                                 ctypes.c_void_p(stream), ctypes.byref(h))
     return st, (h.value or 0)
 
 
@@ -189,7 +203,9 @@ class Qwen3Attention:
     """
 
     def __init__(self, wq, wk, wv, wo, q_norm, k_norm, *, n_q: int, n_kv: int, d_head: int = 128,
-                 eps: float = 1e-6, rope_theta: float = 1e6):
+                 eps: float = 1e-6, rope_theta: float = 1e6, input_norm=None):
+        """input_norm [d] (optional): the handle then computes
+        hidden + block(RMSNorm(hidden) * input_norm) (pre-norm and residual fused)."""
         torch = _torch()
         self.dtype = wq.dtype
         self.d_model = wq.shape[1]
@@ -200,9 +216,16 @@ class Qwen3Attention:
             _ptr(wq, "wq", self.dtype, (hq, d)), _ptr(wk, "wk", self.dtype, (hkv, d)),
             _ptr(wv, "wv", self.dtype, (hkv, d)), _ptr(wo, "wo", self.dtype, (d, hq)),
             _ptr(q_norm, "q_norm", self.dtype, (d_head,)), _ptr(k_norm, "k_norm", self.dtype, (d_head,)))
-        st, self.handle = qwen3_attn_create(self.desc, self.weights, torch.cuda.current_stream().cuda_stream)
+        stream = torch.cuda.current_stream().cuda_stream
+        if input_norm is None:
+            st, self.handle = qwen3_attn_create(self.desc, self.weights, stream)
+            name = "qwen3_attn_create"
+        else:
+            st, self.handle = qwen3_attn_create_with_input_norm(
+                self.desc, self.weights, _ptr(input_norm, "input_norm", self.dtype, (d,)), stream)
+            name = "qwen3_attn_create_with_input_norm"
         if st != 0:
-            raise Qwen3AttnError("qwen3_attn_create", st)
+            raise Qwen3AttnError(name, st)
         self._ws = None
 
     def close(self):

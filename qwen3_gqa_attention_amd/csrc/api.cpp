@@ -22,6 +22,7 @@ struct qwen3_attn {
   float* inv_freq;   // [128]: omega_i / (2 pi) as hi [0..63] + lo [64..127] floats,
                      // omega_i = theta^(-2i/128)
   float inv_freq_host[128];
+  int in_norm;       // 1: forward = hidden + block(RMSNorm(hidden) * input gain)
   // measurement aid: events before each kernel and after the last
   int timing_cap;
   int timing_count;
@@ -141,7 +142,8 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
-                    d.n_q, d.n_kv, kv, T_len, 0, d.eps, past, q3::kScoreScaleLog2};
+                    d.n_q, d.n_kv, kv, T_len, 0, d.eps, past,
+                    h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2};
   mark(h, s, 0);
   hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, M, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
@@ -156,7 +158,8 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
-                              M, d.d_model, hq, s, nullptr);
+                              M, d.d_model, hq, s, nullptr,
+                              h->in_norm ? reinterpret_cast<const T*>(hidden) : nullptr);
   mark_done(h, s);
   return hip_status(r);
 }
@@ -172,7 +175,8 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
-                    d.n_q, d.n_kv, kv, 1, 1, d.eps, nullptr, q3::kScoreScaleLog2};
+                    d.n_q, d.n_kv, kv, 1, 1, d.eps, nullptr,
+                    h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2};
   mark(h, s, 0);
   float* part = L.part ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
   hipError_t r = hipSuccess;
@@ -194,7 +198,8 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
-                              N, d.d_model, hq, s, part);
+                              N, d.d_model, hq, s, part,
+                              h->in_norm ? reinterpret_cast<const T*>(hidden) : nullptr);
   mark_done(h, s);
   return hip_status(r);
 }
@@ -205,12 +210,8 @@ qwen3_attn_status check_handle_device(const qwen3_attn_t* h) {
   return dev == h->device ? QWEN3_ATTN_OK : QWEN3_ATTN_EINVAL;
 }
 
-}  // namespace
-
-extern "C" {
-
-qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc, const qwen3_attn_weights* w,
-                                    void* stream, qwen3_attn_t** out) {
+qwen3_attn_status create_impl(const qwen3_attn_desc* desc, const qwen3_attn_weights* w,
+                              const void* input_norm, void* stream, qwen3_attn_t** out) {
   if (!out) return QWEN3_ATTN_EINVAL;
   *out = nullptr;
   qwen3_attn_status st = check_desc(desc);
@@ -261,6 +262,17 @@ qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc, const qwen3_att
   if (r == hipSuccess) r = hipMemcpyAsync(h->g_k, w->k_norm, 128 * es, hipMemcpyDeviceToDevice, s);
   if (r == hipSuccess)
     r = hipMemcpyAsync(h->inv_freq, h->inv_freq_host, 128 * sizeof(float), hipMemcpyHostToDevice, s);
+  // Input RMSNorm: (x / rms(x) * g) W^T = (x W'^T) / rms(x) with W' = W * g by
+  // columns, so the gain is folded into the q/k/v weights once here.
+  h->in_norm = input_norm != nullptr;
+  if (r == hipSuccess && input_norm) {
+    const int rows = (desc->n_q + 2 * desc->n_kv) * 128, cols = desc->d_model;
+    r = desc->dtype == QWEN3_ATTN_F32
+            ? q3::launch_scale_columns<float>(static_cast<float*>(h->w_qkv), rows, cols,
+                                              static_cast<const float*>(input_norm), s)
+            : q3::launch_scale_columns<q3::bf16_t>(static_cast<q3::bf16_t*>(h->w_qkv), rows, cols,
+                                                   static_cast<const q3::bf16_t*>(input_norm), s);
+  }
   if (r == hipSuccess) r = hipStreamSynchronize(s);  // host staging of inv_freq must complete
   if (r != hipSuccess) {
     (void)hipFree(h->mem);
@@ -269,6 +281,25 @@ qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc, const qwen3_att
   }
   *out = h;
   return QWEN3_ATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc, const qwen3_attn_weights* w,
+                                    void* stream, qwen3_attn_t** out) {
+  return create_impl(desc, w, nullptr, stream, out);
+}
+
+qwen3_attn_status qwen3_attn_create_with_input_norm(const qwen3_attn_desc* desc,
+                                                    const qwen3_attn_weights* w,
+                                                    const void* input_norm, void* stream,
+                                                    qwen3_attn_t** out) {
+  if (!input_norm) {
+    if (out) *out = nullptr;
+    return QWEN3_ATTN_EINVAL;
+  }
+  return create_impl(desc, w, input_norm, stream, out);
 }
 
 size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode, int32_t B_or_N,

@@ -35,7 +35,18 @@ namespace q3 {
 struct StoreEpilogue {
   void* c;
   int ldc;
+  const void* residual;  // non-null: C = residual + A W^T (same layout as C), added in fp32
 };
+
+// Sum of squares of an operand fragment (for the per-row RMS of the input).
+__device__ __forceinline__ float frag_sumsq(const bf16x8_v& a, float acc) {
+  bf16x2_v p[4];
+  __builtin_memcpy(p, &a, 16);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2_f32_bf16(p[e], p[e], acc, false);
+  return acc;
+}
+__device__ __forceinline__ float frag_sumsq(float a, float acc) { return fmaf(a, a, acc); }
 
 constexpr int kXcds = 8;
 
@@ -98,8 +109,12 @@ __device__ __forceinline__ int swz(int row, int k) {
   return row * (8 * EPC) + ((((k / EPC) ^ (row >> 1)) & 7) * EPC) + (k % EPC);
 }
 
+// NORM (q/k/v only): the input rows are RMS-normalised on the fly -- the
+// gain is folded into the weights, and the sum of squares of each A row is
+// accumulated from the A fragments the MFMAs consume, so 1/rms(row) scales
+// the accumulators in the epilogue.
 template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false,
-          int NSTAGE = 2>
+          int NSTAGE = 2, bool NORM = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restrict__ A,
                                                                 const T* __restrict__ B, int M,
                                                                 int N, int K, QkvEpilogue qe,
@@ -180,6 +195,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
   };
 
   f32x16_v acc[MI][NI];
+  float ssq[MI];  // NORM: this lane's part of the sum of squares of its A rows
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) ssq[mi] = 0.f;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -229,6 +247,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = MF::run(af[ks & 1][mi], bfr[ks & 1][ni], acc[mi][ni]);
+      if constexpr (NORM) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) ssq[mi] = frag_sumsq(af[ks & 1][mi], ssq[mi]);
+      }
       // Pin the order the scheduler would otherwise undo: each MFMA of this
       // step is followed by one LDS read of the next step.
       constexpr int NR = MI + NI, NM = MI * NI;
@@ -263,6 +285,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
         }
       }
     return;
+  }
+  if constexpr (NORM) {
+    // Lane l holds half of row (l % 32)'s sum of squares; the accumulator
+    // element i of lane l belongs to row mfma32_row(i, l).
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ssq[mi]),
+                                                       __float_as_uint(ssq[mi]), false, false);
+      const float full = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float ss = __shfl(full, mfma32_row(i, lane), kWave);
+        const float rs = rsqrtf(ss / (float)K + qe.eps);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni][i] *= rs;
+      }
+    }
+  }
+  if constexpr (!QKV) {
+    if (se.residual) {
+      const T* res = reinterpret_cast<const T*>(se.residual);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni][i] += to_f32<T>(res[(size_t)row * se.ldc + n0 + wn * 32 * NI + ni * 32 + c32]);
+        }
+    }
   }
   int head = 0, kind = 3;  // kind 3: plain projection output
   if constexpr (QKV) {
@@ -362,13 +415,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 }
 
 template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false,
-          int NSTAGE = 2>
+          int NSTAGE = 2, bool NORM = false>
 static hipError_t launch_gemm(const T* A, const T* B, int M, int N, int K, const QkvEpilogue& qe,
                               const StoreEpilogue& se, hipStream_t s, int ksplit = 1) {
   constexpr int BM = 32 * MI * WM;
   constexpr int BN = 32 * NI * WN;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV, PARTIAL, NSTAGE>), dim3(tiles, ksplit),
+  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV, PARTIAL, NSTAGE, NORM>), dim3(tiles, ksplit),
                      dim3(WM * WN * 64), 0, s, A, B, M, N, K, qe, se);
   return hipGetLastError();
 }
@@ -403,7 +456,7 @@ int small_m_partial_floats(int M, int N, int K, int es) {
 // evaluated here from positions and omega / (2 pi) (hi + lo floats).
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
-                                                         int M, int N, QkvEpilogue qe,
+                                                         int M, int N, int K, QkvEpilogue qe,
                                                          const float* __restrict__ inv_freq) {
   const int head = blockIdx.x;
   const int tid = threadIdx.x, j = tid & 15;
@@ -423,6 +476,22 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
       v[e] += x0[e];
       v[4 + e] += x1[e];
     }
+  }
+  if (qe.in_norm_x) {
+    // Input RMSNorm (gain folded into the weights): 1/rms of the row of x,
+    // K/16 elements per thread (K is a multiple of 128).
+    const T* xr = reinterpret_cast<const T*>(qe.in_norm_x) + (size_t)r * K;
+    float sx = 0.f;
+    for (int c = j * 8; c < K; c += 128)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xv = to_f32<T>(xr[c + e]);
+        sx = fmaf(xv, xv, sx);
+      }
+    sx = row16_sum(sx);
+    const float rx = rsqrtf(sx / (float)K + qe.eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= rx;
   }
   if (kind != 2) {
     // RMS over the head's 128 columns: 8 per thread, 16 threads per row.
@@ -466,11 +535,16 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
 // out[m][n] = sum over K slices of part[k][m][n], rounded to T.
 template <typename T>
 __global__ __launch_bounds__(64) void sum_partials_kernel(const float* __restrict__ part, int ks,
-                                                          int MN, T* __restrict__ out) {
+                                                          int MN, T* __restrict__ out,
+                                                          const T* __restrict__ residual) {
   const int i = (blockIdx.x * 64 + threadIdx.x) * 4;
   if (i >= MN) return;
   f32x4_v a = *reinterpret_cast<const f32x4_v*>(part + i);
   for (int k = 1; k < ks; ++k) a += *reinterpret_cast<const f32x4_v*>(part + (size_t)k * MN + i);
+  if (residual) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] += to_f32<T>(residual[i + j]);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) out[i + j] = from_f32<T>(a[j]);
 }
@@ -483,34 +557,39 @@ constexpr int kCus = 256;
 template <typename T>
 hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const QkvEpilogue& e,
                            hipStream_t s, float* part, const float* inv_freq) {
-  StoreEpilogue se{nullptr, 0};
+  StoreEpilogue se{nullptr, 0, nullptr};
   if (M <= kSmallM && part) {
     const int ks = small_m_ksplit<T>(N, K);
-    StoreEpilogue ps{part, N};
+    StoreEpilogue ps{part, N, nullptr};
     hipError_t r = launch_gemm<T, 2, 1, 1, 4, false, true>(X, Wqkv, M, N, K, e, ps, s, ks);
     if (r != hipSuccess) return r;
     hipLaunchKernelGGL(qkv_finish_kernel<T>, dim3(N / kHeadDim, (M + 15) / 16), dim3(256), 0, s,
-                       part, ks, M, N, e, inv_freq);
+                       part, ks, M, N, K, e, inv_freq);
     return hipGetLastError();
   }
-  if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
+  const bool norm = e.in_norm_x != nullptr;
+  if (M <= 64)
+    return norm ? launch_gemm<T, 2, 1, 1, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
+                : launch_gemm<T, 2, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
   if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus)
-    return launch_gemm<T, 4, 2, 2, 4, true>(X, Wqkv, M, N, K, e, se, s);
-  return launch_gemm<T, 4, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
+    return norm ? launch_gemm<T, 4, 2, 2, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
+                : launch_gemm<T, 4, 2, 2, 4, true>(X, Wqkv, M, N, K, e, se, s);
+  return norm ? launch_gemm<T, 4, 1, 1, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
+              : launch_gemm<T, 4, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
 }
 
 template <typename T>
 hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, hipStream_t s,
-                            float* part) {
+                            float* part, const T* residual) {
   QkvEpilogue qe{};
-  StoreEpilogue se{C, N};
+  StoreEpilogue se{C, N, residual};
   if (M <= kSmallM && part) {
     const int ks = small_m_ksplit<T>(N, K);
-    StoreEpilogue ps{part, N};
+    StoreEpilogue ps{part, N, nullptr};
     hipError_t r = launch_gemm<T, 2, 1, 1, 4, false, true>(A, W, M, N, K, qe, ps, s, ks);
     if (r != hipSuccess) return r;
     hipLaunchKernelGGL(sum_partials_kernel<T>, dim3((M * N / 4 + 63) / 64), dim3(64), 0, s, part,
-                       ks, M * N, C);
+                       ks, M * N, C, residual);
     return hipGetLastError();
   }
   if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, false>(A, W, M, N, K, qe, se, s);
@@ -528,8 +607,26 @@ template hipError_t launch_qkv_gemm<float>(const float*, const float*, int, int,
 template hipError_t launch_qkv_gemm<bf16_t>(const bf16_t*, const bf16_t*, int, int, int,
                                             const QkvEpilogue&, hipStream_t, float*, const float*);
 template hipError_t launch_proj_gemm<float>(const float*, const float*, float*, int, int, int,
-                                            hipStream_t, float*);
+                                            hipStream_t, float*, const float*);
 template hipError_t launch_proj_gemm<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, int, int, int,
-                                             hipStream_t, float*);
+                                             hipStream_t, float*, const bf16_t*);
+
+template <typename T>
+__global__ __launch_bounds__(256) void scale_columns_kernel(T* __restrict__ W, int rows, int cols,
+                                                            const T* __restrict__ g) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * cols) return;
+  W[i] = from_f32<T>(to_f32<T>(W[i]) * to_f32<T>(g[i % cols]));
+}
+
+template <typename T>
+hipError_t launch_scale_columns(T* W, int rows, int cols, const T* g, hipStream_t s) {
+  const size_t n = (size_t)rows * cols;
+  hipLaunchKernelGGL(scale_columns_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     W, rows, cols, g);
+  return hipGetLastError();
+}
+template hipError_t launch_scale_columns<float>(float*, int, int, const float*, hipStream_t);
+template hipError_t launch_scale_columns<bf16_t>(bf16_t*, int, int, const bf16_t*, hipStream_t);
 
 }  // namespace q3

@@ -49,6 +49,8 @@ struct QkvEpilogue {
   float eps;
   const int32_t* past;       // prefill: [seqs] cached tokens before this chunk (slot =
                              // past[seq] + row % T), or null for empty caches
+  const void* in_norm_x;     // non-null: the block's input is RMSNorm(x) (gain folded into
+                             // the weights); x [rows, d] is read to form 1/rms per row
   float q_scale;             // q~ is stored times this (log2(e) / sqrt(d_head): the
                              // attention kernels then take exp2 of raw dot products)
 };
@@ -67,10 +69,16 @@ hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K,
                            const QkvEpilogue& e, hipStream_t s, float* part,
                            const float* inv_freq);
 
-// Plain projection C[M,N] = A[M,K] * W[N,K]^T (o_proj); `part` as above.
+// Plain projection C[M,N] = A[M,K] * W[N,K]^T (o_proj); `part` as above;
+// `residual` (may be null, layout of C) is added in fp32 before rounding.
 template <typename T>
 hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, hipStream_t s,
-                            float* part);
+                            float* part, const T* residual);
+
+// W[r][c] *= g[c] for a [rows, cols] matrix (folds an input RMSNorm gain
+// into the projection weights).
+template <typename T>
+hipError_t launch_scale_columns(T* W, int rows, int cols, const T* g, hipStream_t s);
 
 // fp32 scratch (floats) the split-K path of an M <= 64 projection needs.
 int small_m_partial_floats(int M, int N, int K, int elem_size);

@@ -55,6 +55,14 @@ def test_create_rejects_bad_descriptors_before_any_hip_call(built_lib, kw, statu
     assert st == status and h == 0
 
 
+def test_create_with_input_norm_rejects_null_gain(built_lib):
+    h = ctypes.c_void_p(1)
+    st = q3.lib().qwen3_attn_create_with_input_norm(ctypes.byref(desc()),
+                                                    ctypes.byref(q3.Qwen3AttnWeights(*([0x1000] * 6))),
+                                                    None, None, ctypes.byref(h))
+    assert st == 1 and not h.value
+
+
 def test_create_rejects_null_weights(built_lib):
     for i in range(6):
         ptrs = [0x1000] * 6

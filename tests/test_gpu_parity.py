@@ -355,6 +355,68 @@ def test_decode_full_size_sampled_sequences():
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------- input RMSNorm + residual fused
+def layer_block(inp, w, g_in):
+    import qwen3_gqa_attention_amd as q3m
+    return q3m.Qwen3Attention(dev(inp["Wq"], w.dtype), dev(inp["Wk"], w.dtype), dev(inp["Wv"], w.dtype),
+                              dev(inp["Wo"], w.dtype), dev(inp["gq"], w.dtype), dev(inp["gk"], w.dtype),
+                              n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA,
+                              input_norm=dev(g_in, w.dtype))
+
+
+def input_gain(w, d, seed):
+    from workloads import bf16_bits_to_f32, round_to_bf16_bits
+    g = (1 + 0.1 * np.random.default_rng(seed).standard_normal(d)).astype(np.float32)
+    return bf16_bits_to_f32(round_to_bf16_bits(g)) if w.dtype == "bf16" else g
+
+
+@pytest.mark.parametrize("idx,B,T", [(1, 1, 128), (2, 2, 300), (4, 1, 100), (2, 1, 40)])
+def test_layer_prefill_parity(idx, B, T):
+    import torch
+    w = WORKLOADS[idx]
+    say(f"layer prefill parity (input norm + residual): {w.name} B={B} T={T}")
+    inp = prefill_inputs(w, B=B, T=T)
+    g_in = input_gain(w, w.d, 7 + idx)
+    blk = layer_block(inp, w, g_in)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    kc = torch.full((B, w.n_kv, T + 8, 128), float("nan"), dtype=x.dtype, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    y = blk.prefill(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_residual(inp["X"], g_in, inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"],
+                                  inp["gq"], inp["gk"], inp["positions"], n_q=w.n_q, n_kv=w.n_kv,
+                                  eps=EPS, theta=ROPE_THETA)
+    assert_close(host(kc)[:, :, :T], ref["Kc"], w.dtype, "k cache")
+    assert_close(host(vc)[:, :, :T], ref["Vc"], w.dtype, "v cache")
+    assert_close(host(y), ref["Y"], w.dtype, "layer output x + block(norm(x))")
+    blk.close()
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 8), ("f32", 8), ("bf16", 100)])
+def test_layer_decode_parity(dtype, N):
+    import torch
+    w = dataclasses.replace(WORKLOADS[5], dtype=dtype)
+    say(f"layer decode parity: dtype={dtype} N={N}")
+    lens = (np.arange(N, dtype=np.int32) * 131) % 2000
+    inp = decode_inputs(w, N=N)
+    inp["positions"] = lens
+    cap = 2048
+    kc, vc = decode_cache_host(w, lens, cap)
+    g_in = input_gain(w, w.d, 17)
+    blk = layer_block(inp, w, g_in)
+    kcd, vcd = dev(kc, w.dtype), dev(vc, w.dtype)
+    y = blk.decode(dev(inp["X"], w.dtype), torch.from_numpy(lens).to("cuda"), kcd, vcd)
+    torch.cuda.synchronize()
+    ref = oracle.decode_residual(inp["X"], g_in, inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"],
+                                 inp["gq"], inp["gk"], lens, kc, vc, n_q=w.n_q, n_kv=w.n_kv,
+                                 eps=EPS, theta=ROPE_THETA)
+    assert_close(host(y), ref["Y"], w.dtype, "layer decode output")
+    kh = host(kcd)
+    assert_close(np.stack([kh[s, :, lens[s]] for s in range(N)]), ref["k_new"], w.dtype, "new k")
+    blk.close()
+
+
 # --------------------------------------------------------------------- paged KV
 def to_paged(kc, vc, lengths, bs, *, seed=0, spare=3):
     """Scatter contiguous host caches [S, n_kv, cap, dh] into pools
