@@ -31,6 +31,11 @@ design notes):
   * The attention is causal by token index: a query that is the i-th of T new
     tokens over S keys sees keys 0 .. S-T+i ([BUILD] "The complete code",
     the tril(diagonal=S-T) mask).  Positions drive RoPE only.
+  * A sliding-window layer of window W ([HF] "Layer 1 - Qwen3Model" and
+    "Layer 3 - Qwen3Attention": the per-layer sliding_window attribute and
+    the sliding-window causal mask) keeps the W most recent keys, the query's
+    own included: query i of the tril mask above sees keys j with
+    S-T+i-W < j <= S-T+i.  The cache still holds every key.
   * cos/sin are not multiplied by any attention_scaling factor (default RoPE).
   * eps sits inside the square root; a zero head vector maps to zero.
   * The oracle is the exact math on the given inputs; it does not emulate the
@@ -115,18 +120,22 @@ def softmax(s: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+def gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window=None) -> np.ndarray:
     """Causal GQA for one sequence.
 
     q: [T, n_q, dh] queries (the last T of S positions);
     k, v: [S, n_kv, dh] keys/values for positions 0 .. S-1 (S >= T).
     Returns [T, n_q, dh].  Query head h reads KV head h // (n_q // n_kv);
-    query i sees keys j <= S - T + i.
+    query i sees keys j <= S - T + i, and with a sliding window W (None or
+    0: no window) only those with j > S - T + i - W.
     """
     T, n_q, dh = q.shape
     S, n_kv, _ = k.shape
     n_rep = n_q // n_kv
-    visible = np.arange(S)[None, :] <= (S - T + np.arange(T))[:, None]     # [T, S]
+    last = (S - T + np.arange(T))[:, None]                                  # [T, 1]
+    visible = np.arange(S)[None, :] <= last                                 # [T, S]
+    if window:
+        visible &= np.arange(S)[None, :] > last - window
     out = np.empty_like(q)
     for h in range(n_q):
         g = h // n_rep
@@ -160,8 +169,9 @@ def project_norm_rope(x, wq, wk, wv, gq, gk, positions, *, n_q, n_kv, dh, eps,
 
 
 def prefill(x, wq, wk, wv, wo, gq, gk, positions, *, n_q, n_kv, dh=128,
-            eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
-    """Block forward over B sequences of T new tokens with an empty cache.
+            eps=1e-6, theta=1e6, dtype=np.float64, window=None) -> dict:
+    """Block forward over B sequences of T new tokens with an empty cache
+    (window: the sliding window of the layer, None for full attention).
 
     x: [B, T, d]; positions: [B, T].  Returns a dict with
       Y  [B, T, d]        block output,
@@ -173,7 +183,7 @@ def prefill(x, wq, wk, wv, wo, gq, gk, positions, *, n_q, n_kv, dh=128,
     q, k, v = project_norm_rope(x, wq, wk, wv, gq, gk, positions, n_q=n_q,
                                 n_kv=n_kv, dh=dh, eps=eps, theta=theta, dtype=dtype)
     B = q.shape[0]
-    a = np.stack([gqa_attention(q[b], k[b], v[b]) for b in range(B)])
+    a = np.stack([gqa_attention(q[b], k[b], v[b], window) for b in range(B)])
     A = merge_heads(a)
     Y = linear(A, wo, dtype)
     return dict(Y=Y, Q=q, Kc=np.transpose(k, (0, 2, 1, 3)),
@@ -181,14 +191,15 @@ def prefill(x, wq, wk, wv, wo, gq, gk, positions, *, n_q, n_kv, dh=128,
 
 
 def decode(x, wq, wk, wv, wo, gq, gk, positions, k_cache, v_cache, *, n_q, n_kv,
-           dh=128, eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+           dh=128, eps=1e-6, theta=1e6, dtype=np.float64, window=None) -> dict:
     """One new token per sequence on top of an existing cache.
 
     x: [N, d]; positions[s] = L_s, the number of cached tokens of sequence s;
     k_cache, v_cache: [N, n_kv, >=L_s, dh] holding post-norm post-RoPE keys
     and values of positions 0 .. L_s-1.  The new token sits at position L_s
     and sees all L_s + 1 keys ([BUILD] "The complete code": the cache update
-    then the tril(diagonal=S-T) mask with T=1; the generate loop).
+    then the tril(diagonal=S-T) mask with T=1; the generate loop), or the
+    last `window` of them.
     Returns Y [N, d], the new k~ and v [N, n_kv, dh], and A [N, n_q*dh].
     """
     N = x.shape[0]
@@ -201,13 +212,14 @@ def decode(x, wq, wk, wv, wo, gq, gk, positions, k_cache, v_cache, *, n_q, n_kv,
         L = int(pos[s, 0])
         ks = np.concatenate([np.asarray(k_cache[s][:, :L], dtype).transpose(1, 0, 2), k[s]], axis=0)
         vs = np.concatenate([np.asarray(v_cache[s][:, :L], dtype).transpose(1, 0, 2), v[s]], axis=0)
-        A[s] = merge_heads(gqa_attention(q[s], ks, vs))[0]
+        A[s] = merge_heads(gqa_attention(q[s], ks, vs, window))[0]
     Y = linear(A, wo, dtype)
     return dict(Y=Y, k_new=k[:, 0], v_new=v[:, 0], A=A, Q=q[:, 0])
 
 
 def prefill_chunk(x, wq, wk, wv, wo, gq, gk, positions, past_len, k_cache, v_cache, *,
-                  n_q, n_kv, dh=128, eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+                  n_q, n_kv, dh=128, eps=1e-6, theta=1e6, dtype=np.float64,
+                  window=None) -> dict:
     """A chunk of T new tokens per sequence appended to a non-empty cache.
 
     x: [B, T, d]; positions: [B, T]; past_len[b] = P_b cached tokens;
@@ -227,7 +239,7 @@ def prefill_chunk(x, wq, wk, wv, wo, gq, gk, positions, past_len, k_cache, v_cac
         P = int(past_len[b])
         ks = np.concatenate([np.asarray(k_cache[b][:, :P], dtype).transpose(1, 0, 2), k[b]], axis=0)
         vs = np.concatenate([np.asarray(v_cache[b][:, :P], dtype).transpose(1, 0, 2), v[b]], axis=0)
-        out.append(gqa_attention(q[b], ks, vs))
+        out.append(gqa_attention(q[b], ks, vs, window))
     A = merge_heads(np.stack(out))
     Y = linear(A, wo, dtype)
     return dict(Y=Y, Q=q, Kc=np.transpose(k, (0, 2, 1, 3)),
@@ -235,30 +247,30 @@ def prefill_chunk(x, wq, wk, wv, wo, gq, gk, positions, past_len, k_cache, v_cac
 
 
 def prefill_residual(x, g_in, wq, wk, wv, wo, gq, gk, positions, *, n_q, n_kv, dh=128,
-                     eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+                     eps=1e-6, theta=1e6, dtype=np.float64, window=None) -> dict:
     """The attention half of a decoder layer: x + block(RMSNorm(x) * g_in)
     ([BUILD] "The complete code": input_layernorm, self-attention, residual
     add).  Same arguments as prefill plus the input-norm gain g_in [d];
     returns prefill's dict with Y replaced by the layer output."""
     xd = np.asarray(x, dtype)
     out = prefill(rms_norm(xd, g_in, eps), wq, wk, wv, wo, gq, gk, positions, n_q=n_q,
-                  n_kv=n_kv, dh=dh, eps=eps, theta=theta, dtype=dtype)
+                  n_kv=n_kv, dh=dh, eps=eps, theta=theta, dtype=dtype, window=window)
     out["Y"] = xd + out["Y"]
     return out
 
 
 def decode_residual(x, g_in, wq, wk, wv, wo, gq, gk, positions, k_cache, v_cache, *, n_q,
-                    n_kv, dh=128, eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+                    n_kv, dh=128, eps=1e-6, theta=1e6, dtype=np.float64, window=None) -> dict:
     """decode() with the input RMSNorm and the residual add around the block."""
     xd = np.asarray(x, dtype)
     out = decode(rms_norm(xd, g_in, eps), wq, wk, wv, wo, gq, gk, positions, k_cache, v_cache,
-                 n_q=n_q, n_kv=n_kv, dh=dh, eps=eps, theta=theta, dtype=dtype)
+                 n_q=n_q, n_kv=n_kv, dh=dh, eps=eps, theta=theta, dtype=dtype, window=window)
     out["Y"] = xd + out["Y"]
     return out
 
 
 def prefill_rows(x, wq, wk, wv, wo, gq, gk, positions, rows, *, n_q, n_kv, dh=128,
-                 eps=1e-6, theta=1e6, dtype=np.float64) -> dict:
+                 eps=1e-6, theta=1e6, dtype=np.float64, window=None) -> dict:
     """The prefill output at selected tokens only, for full-size checks.
 
     rows: list of (b, t).  Same definition as ``prefill``: keys/values of
@@ -282,7 +294,7 @@ def prefill_rows(x, wq, wk, wv, wo, gq, gk, positions, rows, *, n_q, n_kv, dh=12
                                     positions[b, t:t + 1], n_q=n_q, n_kv=0, dh=dh,
                                     eps=eps, theta=theta, dtype=dtype)
         k, v = kv[b]
-        A[i] = merge_heads(gqa_attention(q, k[:t + 1], v[:t + 1]))[0]
+        A[i] = merge_heads(gqa_attention(q, k[:t + 1], v[:t + 1], window))[0]
     Y = linear(A, wo, dtype)
     return dict(Y=Y, A=A, Kc={b: np.transpose(kv[b][0], (1, 0, 2)) for b in seqs},
                 Vc={b: np.transpose(kv[b][1], (1, 0, 2)) for b in seqs})

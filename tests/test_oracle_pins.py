@@ -399,6 +399,92 @@ def test_layer_decode_equals_last_layer_prefill_row():
     np.testing.assert_allclose(dec["Y"], full["Y"][:, 8], rtol=1e-12, atol=1e-13)
 
 
+# --- sliding window ------------------------------------------------------
+# A layer with sliding window W keeps the W most recent keys, the query's own
+# included ("Qwen3 Architecture Layer-by-Layer", sections "Layer 1 -
+# Qwen3Model" and "Layer 3 - Qwen3Attention": per-layer sliding_window and
+# the sliding-window causal mask).
+def test_window_one_attends_to_own_value_only():
+    # W = 1: every token sees only itself, so A_t = concat_h V_{t, h // n_rep}
+    # and Y_t = Wo . A_t (a window one key too wide or too narrow fails).
+    p = rand_block(31, B=2, T=7, d=48, n_q=6, n_kv=3)
+    out = run_prefill(p, window=1)
+    v = (p["x"] @ p["wv"].T).reshape(2, 7, 3, 16)
+    cat = np.concatenate([v[:, :, h // 2] for h in range(6)], axis=-1)
+    np.testing.assert_allclose(out["A"], cat, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(out["Y"], cat @ p["wo"].T, rtol=1e-12, atol=1e-13)
+
+
+def test_window_covering_the_sequence_is_full_attention():
+    p = rand_block(32, B=2, T=9)
+    full = run_prefill(p)
+    for W in (9, 10, 100):
+        np.testing.assert_array_equal(run_prefill(p, window=W)["Y"], full["Y"])
+    assert not np.allclose(run_prefill(p, window=8)["Y"][:, 8], full["Y"][:, 8])
+    np.testing.assert_array_equal(run_prefill(p, window=8)["Y"][:, :8], full["Y"][:, :8])
+
+
+@pytest.mark.parametrize("W", [2, 3, 5])
+def test_window_row_equals_full_prefill_of_the_window_slice(W):
+    # RoPE scores depend on position differences only, so row t of a window-W
+    # prefill equals the last row of a plain causal prefill of tokens
+    # t-W+1 .. t that keep their own positions.
+    p = rand_block(33 + W, B=1, T=10)
+    win = run_prefill(p, window=W)
+    for t in range(10):
+        lo = max(0, t - W + 1)
+        sl = run_prefill({**p, "x": p["x"][:, lo:t + 1], "positions": p["positions"][:, lo:t + 1]})
+        np.testing.assert_allclose(win["Y"][:, t], sl["Y"][:, -1], rtol=1e-11, atol=1e-12)
+
+
+def test_window_outputs_do_not_depend_on_tokens_outside_it():
+    # Perturbing token j changes outputs j .. j+W-1 only; rows from j+W on are
+    # bitwise unchanged (and rows before j by causality).
+    p = rand_block(37, B=1, T=12)
+    W = 4
+    base = run_prefill(p, window=W)["Y"]
+    for j in (0, 3, 7):
+        x = p["x"].copy()
+        x[:, j] += np.random.default_rng(j).standard_normal(x.shape[-1])
+        out = run_prefill({**p, "x": x}, window=W)["Y"]
+        np.testing.assert_array_equal(out[:, :j], base[:, :j])
+        np.testing.assert_array_equal(out[:, j + W:], base[:, j + W:])
+        for t in range(j, min(j + W, 12)):
+            assert not np.allclose(out[:, t], base[:, t])
+
+
+def test_window_matches_torch_sdpa_with_band_mask():
+    rng = np.random.default_rng(38)
+    T, S, W = 5, 11, 3
+    q = rng.standard_normal((T, 8, 32))
+    k = rng.standard_normal((S, 2, 32))
+    v = rng.standard_normal((S, 2, 32))
+    ours = oracle.gqa_attention(q, k, v, window=W)
+    tq, tk, tv = (torch.from_numpy(a).permute(1, 0, 2)[None] for a in (q, k, v))
+    band = torch.ones(T, S, dtype=torch.bool)
+    mask = band.tril(diagonal=S - T) & ~band.tril(diagonal=S - T - W)
+    ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, enable_gqa=True)
+    np.testing.assert_allclose(ours, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_window_chunk_and_decode_equal_one_shot_window_prefill():
+    # The window is anchored at the key position P + t of a chunk token, not
+    # at its index inside the chunk; decode is the one-token chunk.
+    p = rand_block(39, B=2, T=13)
+    W = 4
+    full = run_prefill(p, window=W)
+    for P in (2, 6, 12):
+        head = run_prefill({**p, "x": p["x"][:, :P], "positions": p["positions"][:, :P]})
+        ch = oracle.prefill_chunk(**chunk_args(p, P, 13, [P, P], head["Kc"], head["Vc"]),
+                                  window=W)
+        np.testing.assert_allclose(ch["Y"], full["Y"][:, P:], rtol=1e-12, atol=1e-13)
+    head = run_prefill({**p, "x": p["x"][:, :12], "positions": p["positions"][:, :12]})
+    dec = oracle.decode(p["x"][:, 12], p["wq"], p["wk"], p["wv"], p["wo"], p["gq"], p["gk"],
+                        np.array([12, 12]), head["Kc"], head["Vc"], n_q=p["n_q"],
+                        n_kv=p["n_kv"], dh=16, window=W)
+    np.testing.assert_allclose(dec["Y"], full["Y"][:, 12], rtol=1e-12, atol=1e-13)
+
+
 def test_decode_ragged_lengths_and_empty_cache():
     # Sequences with different cache lengths, including 0, are independent.
     p = rand_block(16, B=3, T=6)
