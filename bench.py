@@ -272,7 +272,8 @@ def bench_chunk(args, P=1536, T=512):
             "kernels": kernels}
 
 
-def bench_decode(args):
+def bench_decode(args, window=0):
+    """The 64-sequence decode; window > 0 makes it a sliding-window layer."""
     import numpy as np
     import torch
 
@@ -285,7 +286,8 @@ def bench_decode(args):
     bf = torch.bfloat16
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(bf)
     blk = q3.Qwen3Attention(d(inp["Wq"]), d(inp["Wk"]), d(inp["Wv"]), d(inp["Wo"]), d(inp["gq"]),
-                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA)
+                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA,
+                            sliding_window=window)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(w.seed)
     kc = torch.empty((w.B, w.n_kv, w.cap, 128), dtype=bf, device="cuda")
@@ -316,8 +318,10 @@ def bench_decode(args):
     blk.close()
     step_s = (t1 - t0) / steps
     # algorithmic bytes: each cached key/value row read once (bf16), plus the
-    # new token's q/k/v/o weights and the small activations
-    kv_read = float(np.sum(L.astype(np.int64))) * 2 * w.n_kv * 128 * 2
+    # new token's q/k/v/o weights and the small activations; a window of W
+    # reads the W - 1 most recent cached rows
+    seen = L.astype(np.int64) if window == 0 else np.minimum(L.astype(np.int64), window - 1)
+    kv_read = float(np.sum(seen)) * 2 * w.n_kv * 128 * 2
     weights = (w.n_q + 2 * w.n_kv) * 128 * w.d * 2 + w.d * w.n_q * 128 * 2
     attn_ms = stage_ms[1] / max(ncalls, 1)
     attn_bytes = kv_read + w.B * w.n_kv * 2 * 128 * 2 + 2 * w.B * w.n_q * 128 * 2
@@ -479,6 +483,19 @@ def main():
                          "frac": dd["attn_bytes"] / (dd["attn_ms"] / 1e3) / PEAK_HBM_BYTES,
                          "traffic": traffic.get("decode_attention")},
         }
+    dec_window = None
+    if not args.no_decode:
+        W = 4096
+        log(f"bench: decode, the same 64 sequences in a sliding-window layer (W={W})")
+        dw = bench_decode(args, window=W)
+        nbytes = dw["kv_read"] + dw["weights"]
+        dec_window = {"workload": f"{dw['w'].name}-window{W}", "window": W,
+                      "ms_per_step": dw["step_s"] * 1e3, "tokens_per_s": dw["N"] / dw["step_s"],
+                      "bytes_per_step": nbytes, "GBps": nbytes / dw["step_s"] / 1e9,
+                      "frac_hbm_peak": nbytes / dw["step_s"] / PEAK_HBM_BYTES,
+                      "kernel_ms": dict(zip(q3.STAGES, dw["stage_ms"]))}
+        log(f"bench: window decode {dec_window['ms_per_step']:.4f} ms/step, "
+            f"{dec_window['frac_hbm_peak'] * 100:.1f}% of HBM peak")
     dec_paged = None
     if not args.no_decode:
         log("bench: decode over a paged cache (64-token blocks, shuffled pool)")
@@ -522,6 +539,7 @@ def main():
         "chunked_prefill": chunk,
         "decode": dec,
         "decode_paged": dec_paged,
+        "decode_window": dec_window,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

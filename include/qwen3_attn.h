@@ -58,7 +58,8 @@ typedef enum {
 } qwen3_attn_status;
 
 /* Block configuration.  Supported: d_head == 128; n_q % n_kv == 0;
- * d_model % 128 == 0; n_q / n_kv <= 16 for decode; eps >= 0; rope_theta > 1. */
+ * d_model % 128 == 0; n_q / n_kv <= 16 for decode; eps >= 0; rope_theta > 1;
+ * sliding_window >= 0. */
 typedef struct {
   int32_t d_model;   /* hidden size d */
   int32_t n_q;       /* query heads */
@@ -67,6 +68,15 @@ typedef struct {
   float eps;         /* RMSNorm epsilon of q_norm / k_norm (1e-6 for Qwen3) */
   double rope_theta; /* RoPE base (1e6 for Qwen3) */
   int32_t dtype;     /* a qwen3_attn_dtype */
+  /* 0: full causal attention.  W > 0: a sliding-window layer -- the token at
+   * cache slot i sees only slots i-W+1 .. i, the W most recent keys with its
+   * own ("Qwen3 Architecture Layer-by-Layer", sections "Layer 1 -
+   * Qwen3Model" and "Layer 3 - Qwen3Attention": the per-layer
+   * sliding_window and the sliding-window causal mask).  The caches keep
+   * every key.  Keys older than every window of a call are not read, apart
+   * from the rest of the key tile holding a window's first key (64 keys in
+   * prefill, 16 in decode). */
+  int32_t sliding_window;
 } qwen3_attn_desc;
 
 /* Device pointers, row-major [out, in] as stored in the checkpoints:

@@ -30,7 +30,8 @@ STAGES = ("qkv_norm_rope_gemm", "attention", "o_proj_gemm")
 class Qwen3AttnDesc(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
                 ("d_head", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32)]
+                ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32),
+                ("sliding_window", ctypes.c_int32)]
 
 
 class Qwen3AttnWeights(ctypes.Structure):
@@ -203,14 +204,17 @@ class Qwen3Attention:
     """
 
     def __init__(self, wq, wk, wv, wo, q_norm, k_norm, *, n_q: int, n_kv: int, d_head: int = 128,
-                 eps: float = 1e-6, rope_theta: float = 1e6, input_norm=None):
+                 eps: float = 1e-6, rope_theta: float = 1e6, input_norm=None,
+                 sliding_window: int = 0):
         """input_norm [d] (optional): the handle then computes
-        hidden + block(RMSNorm(hidden) * input_norm) (pre-norm and residual fused)."""
+        hidden + block(RMSNorm(hidden) * input_norm) (pre-norm and residual fused).
+        sliding_window W > 0: each token sees only its W most recent keys."""
         torch = _torch()
         self.dtype = wq.dtype
         self.d_model = wq.shape[1]
         self.n_q, self.n_kv, self.d_head = n_q, n_kv, d_head
-        self.desc = Qwen3AttnDesc(self.d_model, n_q, n_kv, d_head, eps, rope_theta, _dtype_code(self.dtype))
+        self.desc = Qwen3AttnDesc(self.d_model, n_q, n_kv, d_head, eps, rope_theta,
+                                  _dtype_code(self.dtype), sliding_window)
         d, hq, hkv = self.d_model, n_q * d_head, n_kv * d_head
         self.weights = Qwen3AttnWeights(
             _ptr(wq, "wq", self.dtype, (hq, d)), _ptr(wk, "wk", self.dtype, (hkv, d)),

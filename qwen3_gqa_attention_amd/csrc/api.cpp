@@ -44,6 +44,7 @@ qwen3_attn_status check_desc(const qwen3_attn_desc* d) {
   if (d->n_q % d->n_kv != 0) return QWEN3_ATTN_EINVAL;
   if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return QWEN3_ATTN_EINVAL;
   if (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta)) return QWEN3_ATTN_EINVAL;
+  if (d->sliding_window < 0) return QWEN3_ATTN_EINVAL;
   if (d->d_head != 128) return QWEN3_ATTN_EUNSUPPORTED;
   if (d->d_model % 128 != 0) return QWEN3_ATTN_EUNSUPPORTED;
   if ((int64_t)(d->n_q + 2 * d->n_kv) * 128 > INT_MAX / 2) return QWEN3_ATTN_EUNSUPPORTED;
@@ -154,7 +155,8 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   mark(h, s, 1);
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                   reinterpret_cast<const T*>(v_cache), abuf, B, T_len, d.n_q, d.n_kv,
-                                  kv, past, reinterpret_cast<float*>(ws + L.part_off), s);
+                                  kv, past, d.sliding_window,
+                                  reinterpret_cast<float*>(ws + L.part_off), s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
@@ -194,7 +196,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   mark(h, s, 1);
   r = q3::launch_decode_attn<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                 reinterpret_cast<const T*>(v_cache), positions, abuf, N, d.n_q,
-                                d.n_kv, kv, sc, s);
+                                d.n_kv, kv, d.sliding_window, sc, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),

@@ -17,6 +17,8 @@
 // The four groups, then the four waves, are merged in registers / LDS and one
 // partial (max, sum, weighted values) per chunk is written.  A second kernel
 // merges the chunks of each (sequence, query head).
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -66,11 +68,17 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
                                                           const int32_t* __restrict__ positions,
                                                           float* __restrict__ part_acc,
                                                           float* __restrict__ part_ml, int n_q,
-                                                          int n_kv, KvAddr kv, int nchunk) {
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+                                                          int n_kv, KvAddr kv, int nchunk,
+                                                          int window) {
+  const int g = blockIdx.y, s = blockIdx.z;
   const int nkeys = positions[s] + 1;
+  // Sliding window W (0: none): only the last W keys are visible, and the
+  // grid spans only the chunks a window can overlap, counted from the one
+  // holding the sequence's first visible key.
+  const int klo = window > 0 ? max(0, nkeys - window) : 0;
+  const int c = klo / kDecodeChunk + blockIdx.x;
   const int k0 = c * kDecodeChunk;
-  if (k0 >= nkeys) return;
+  if (k0 >= nkeys || k0 + kDecodeChunk <= klo) return;
   const int k1 = min(k0 + kDecodeChunk, nkeys);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -102,7 +110,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
   const T* Kl = Kc + oct * 8;
   const T* Vl = Vc + oct * 8;
   constexpr int U = kDecodeUnroll;
-  for (int kb = wk0; kb < wk1; kb += 4 * U) {
+  // Iterations stay on the 4U-key grid (one cache-block lookup each); keys
+  // below klo in the first one are masked.
+  for (int kb = max(wk0, klo & ~(4 * U - 1)); kb < wk1; kb += 4 * U) {
     // The 4U keys from kb (a multiple of 4U) lie in one cache block.
     const int64_t r0 = kv.row(s, g, kb);
     RowSlice<T> kr[U], vr[U];
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = kb + grp + 4 * u;
-      val[u] = key < wk1;
+      val[u] = key < wk1 && key >= klo;
       if (val[u]) {
         kr[u].load_stream(Kl + (r0 + grp + 4 * u) * kHeadDim);
         vr[u].load_stream(Vl + (r0 + grp + 4 * u) * kHeadDim);
@@ -207,15 +217,17 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
                                                              const float* __restrict__ part_ml,
                                                              const int32_t* __restrict__ positions,
                                                              T* __restrict__ Out, int n_q, int n_kv,
-                                                             int nchunk) {
+                                                             int nchunk, int window) {
   constexpr int U = 16;
   const int head = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int n_rep = n_q / n_kv;
   const int g = head / n_rep, r = head % n_rep;
-  const int nc = (positions[s] + 1 + kDecodeChunk - 1) / kDecodeChunk;
+  const int nkeys = positions[s] + 1;
+  const int nc = (nkeys + kDecodeChunk - 1) / kDecodeChunk;
+  const int c_lo = window > 0 ? max(0, nkeys - window) / kDecodeChunk : 0;  // first chunk written
   const size_t base = (size_t)(s * n_kv + g) * nchunk;
   float M = -INFINITY, a = 0.f, lt = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += U) {
+  for (int c0 = c_lo; c0 < nc; c0 += U) {
     float mv[U], lv[U], av[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -244,31 +256,35 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
 
 template <typename T, int NREP>
 static void launch_decode_nrep(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
-                               int N, int n_q, int n_kv, const KvAddr& kv, const DecodeScratch& ws,
-                               hipStream_t s) {
-  hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(ws.nchunk, n_kv, N), dim3(256), 0, s, Q,
-                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, kv, ws.nchunk);
+                               int N, int n_q, int n_kv, const KvAddr& kv, int window,
+                               const DecodeScratch& ws, hipStream_t s) {
+  // a window of W keys overlaps at most ceil(W / chunk) + 1 chunks
+  const int gx = window > 0 ? std::min(ws.nchunk, (window + kDecodeChunk - 1) / kDecodeChunk + 1)
+                            : ws.nchunk;
+  hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(gx, n_kv, N), dim3(256), 0, s, Q,
+                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, kv, ws.nchunk, window);
 }
 
 template <typename T>
 hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
-                              T* Out, int N, int n_q, int n_kv, const KvAddr& kv,
+                              T* Out, int N, int n_q, int n_kv, const KvAddr& kv, int window,
                               const DecodeScratch& ws, hipStream_t s) {
+  if (window < 0) return hipErrorInvalidValue;
   switch (n_q / n_kv) {
-    case 1: launch_decode_nrep<T, 1>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
-    case 2: launch_decode_nrep<T, 2>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
-    case 3: launch_decode_nrep<T, 3>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
-    case 4: launch_decode_nrep<T, 4>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
-    case 5: launch_decode_nrep<T, 5>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
-    case 6: launch_decode_nrep<T, 6>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
-    case 8: launch_decode_nrep<T, 8>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
-    case 16: launch_decode_nrep<T, 16>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, ws, s); break;
+    case 1: launch_decode_nrep<T, 1>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, window, ws, s); break;
+    case 2: launch_decode_nrep<T, 2>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, window, ws, s); break;
+    case 3: launch_decode_nrep<T, 3>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, window, ws, s); break;
+    case 4: launch_decode_nrep<T, 4>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, window, ws, s); break;
+    case 5: launch_decode_nrep<T, 5>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, window, ws, s); break;
+    case 6: launch_decode_nrep<T, 6>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, window, ws, s); break;
+    case 8: launch_decode_nrep<T, 8>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, window, ws, s); break;
+    case 16: launch_decode_nrep<T, 16>(Q, Kc, Vc, positions, N, n_q, n_kv, kv, window, ws, s); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(n_q, N), dim3(kHeadDim), 0, s, ws.part_acc,
-                     ws.part_ml, positions, Out, n_q, n_kv, ws.nchunk);
+                     ws.part_ml, positions, Out, n_q, n_kv, ws.nchunk, window);
   return hipGetLastError();
 }
 
@@ -279,9 +295,9 @@ bool decode_nrep_supported(int n_rep) {
 
 template hipError_t launch_decode_attn<float>(const float*, const float*, const float*,
                                               const int32_t*, float*, int, int, int, const KvAddr&,
-                                              const DecodeScratch&, hipStream_t);
+                                              int, const DecodeScratch&, hipStream_t);
 template hipError_t launch_decode_attn<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
                                                const int32_t*, bf16_t*, int, int, int, const KvAddr&,
-                                               const DecodeScratch&, hipStream_t);
+                                               int, const DecodeScratch&, hipStream_t);
 
 }  // namespace q3

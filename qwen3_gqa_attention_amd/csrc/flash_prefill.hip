@@ -58,7 +58,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             T* __restrict__ Out, int B, int T_len,
                                                             int n_q, int n_kv, KvAddr kv,
                                                             const int32_t* __restrict__ past,
-                                                            int nsplit,
+                                                            int window, int nsplit,
                                                             float* __restrict__ part) {
   using MF = Mfma32<T>;
   constexpr int BN = FlashTile<T>::BN;
@@ -123,11 +123,22 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const bool wave_active = Rw < rows_total;
   const int w_tok_lo = P + min(Rw, rows_total - 1) / n_rep;
   const int w_tok_hi = P + min(Rw + 31, rows_total - 1) / n_rep;
+  // Sliding window W (0: none): key position j is visible to the token at
+  // key position i iff i - W < j <= i.  key_lo is this lane's first visible
+  // key; keys below w_mask_lo are masked for at least one row of the wave.
+  const int key_lo = window > 0 ? tok - window + 1 : 0;
+  const int w_key_lo = window > 0 ? w_tok_lo - window + 1 : 0;
+  const int w_mask_lo = window > 0 ? w_tok_hi - window + 1 : 0;
+  // Key tiles of the workgroup: from the first key its first row sees to the
+  // last key its last row sees.
   const int kmax = P + min(R0 + 127, rows_total - 1) / n_rep;
-  const int ntiles_all = kmax / BN + 1;
+  const int kmin = window > 0 ? max(0, P + R0 / n_rep - window + 1) : 0;
+  const int tl0 = kmin / BN;
+  const int ntiles_all = kmax / BN + 1 - tl0;
   const int per_split = (ntiles_all + nsplit - 1) / nsplit;
-  const int t_lo = min(split * per_split, ntiles_all);
-  const int ntiles = min(t_lo + per_split, ntiles_all) - t_lo;  // this workgroup's key tiles
+  const int s_lo = min(split * per_split, ntiles_all);
+  const int t_lo = tl0 + s_lo;
+  const int ntiles = min(s_lo + per_split, ntiles_all) - s_lo;  // this workgroup's key tiles
 
   // Q^T fragments for the whole d_head, kept in VGPRs.
   typename MF::frag qf[DSTEPS];
@@ -232,7 +243,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   }
 
   auto tile = [&](int kt, int buf) {
-    if (wave_active && kt * BN <= w_tok_hi) {
+    if (wave_active && kt * BN <= w_tok_hi && kt * BN + BN - 1 >= w_key_lo) {
       // S^T = K Q^T - m_run.  Q carries the log2(e)/sqrt(d) factor, so the
       // scores are already in the base-2 units of the exponent.
       // The NKB accumulation chains are interleaved, and each k-step's K
@@ -277,13 +288,16 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
           __builtin_amdgcn_sched_group_barrier(0x008, NKB, 0);
         }
       }
-      // causal mask (only tiles that cross this wave's diagonal), running max
-      if (kt * BN + BN - 1 > w_tok_lo) {
+      // causal mask (only tiles that cross this wave's diagonal) and the
+      // window's lower edge (only tiles that cross it), then the running max
+      if (kt * BN + BN - 1 > w_tok_lo || kt * BN < w_mask_lo) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kt * BN + kb * 32 + mfma32_row(i, lane) > tok) s[kb][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt * BN + kb * 32 + mfma32_row(i, lane);
+            if (key > tok || key < key_lo) s[kb][i] = -INFINITY;
+          }
       }
       // Tile max relative to the running max; the two half-waves hold the
       // two halves of each query's keys.
@@ -526,8 +540,8 @@ size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv) {
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
                                 int n_q, int n_kv, const KvAddr& kv, const int32_t* past,
-                                float* part,
-                                hipStream_t s) {
+                                int window, float* part, hipStream_t s) {
+  if (window < 0) return hipErrorInvalidValue;
   const int nsplit = flash_splits(B, T_len, n_q, n_kv);
   if (nsplit > 1 && !part) return hipErrorInvalidValue;
   // Few workgroups: split each query tile's key range over two wave groups
@@ -536,10 +550,10 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
   const int wgs = flash_query_wgs(B, T_len, n_q, n_kv) * nsplit;
   if (wgs < 4 * 256)
     hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, kv, past, nsplit, part);
+                       T_len, n_q, n_kv, kv, past, window, nsplit, part);
   else
     hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, kv, past, nsplit, part);
+                       T_len, n_q, n_kv, kv, past, window, nsplit, part);
   if (nsplit > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -552,9 +566,9 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
 
 template hipError_t launch_flash_prefill<float>(const float*, const float*, const float*, float*,
                                                 int, int, int, int, const KvAddr&,
-                                                const int32_t*, float*, hipStream_t);
+                                                const int32_t*, int, float*, hipStream_t);
 template hipError_t launch_flash_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
                                                  bf16_t*, int, int, int, int, const KvAddr&,
-                                                 const int32_t*, float*, hipStream_t);
+                                                 const int32_t*, int, float*, hipStream_t);
 
 }  // namespace q3

@@ -85,19 +85,21 @@ int small_m_partial_floats(int M, int N, int K, int elem_size);
 
 // Causal GQA flash attention of a T_len-token chunk over the caches, which
 // hold past[b] earlier tokens of sequence b followed by the chunk (past may
-// be null: empty caches).
+// be null: empty caches).  window > 0 limits each token to the `window`
+// most recent keys, its own included (0: full causal attention).
 // `part`: fp32 scratch of flash_partial_floats(...) floats (may be null when
 // that is 0): with few query tiles the key ranges are split over more
 // workgroups and merged by a second kernel.
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
                                 int n_q, int n_kv, const KvAddr& kv, const int32_t* past,
-                                float* part, hipStream_t s);
+                                int window, float* part, hipStream_t s);
 int flash_splits(int B, int T_len, int n_q, int n_kv);
 size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv);
 
 // Split-K decode attention: partial (max, sum, weighted values) per key chunk,
-// then the log-sum-exp merge into Out [N, n_q*128].
+// then the log-sum-exp merge into Out [N, n_q*128].  window > 0: the new
+// token sees only its `window` most recent keys (0: all of them).
 struct DecodeScratch {
   float* part_acc;  // [N, n_kv, nchunk, n_rep, 128]
   float* part_ml;   // [N, n_kv, nchunk, n_rep, 2]
@@ -108,7 +110,7 @@ int decode_chunk_keys();
 bool decode_nrep_supported(int n_rep);
 template <typename T>
 hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
-                              T* Out, int N, int n_q, int n_kv, const KvAddr& kv,
+                              T* Out, int N, int n_q, int n_kv, const KvAddr& kv, int window,
                               const DecodeScratch& ws, hipStream_t s);
 
 }  // namespace q3

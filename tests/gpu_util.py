@@ -37,10 +37,11 @@ def host(t) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def block_from_inputs(inp, n_q, n_kv, dtype) -> q3.Qwen3Attention:
+def block_from_inputs(inp, n_q, n_kv, dtype, **kw) -> q3.Qwen3Attention:
+    """A handle over the workload's weights; kw: further Qwen3Attention options."""
     return q3.Qwen3Attention(dev(inp["Wq"], dtype), dev(inp["Wk"], dtype), dev(inp["Wv"], dtype),
                              dev(inp["Wo"], dtype), dev(inp["gq"], dtype), dev(inp["gk"], dtype),
-                             n_q=n_q, n_kv=n_kv, eps=EPS, rope_theta=ROPE_THETA)
+                             n_q=n_q, n_kv=n_kv, eps=EPS, rope_theta=ROPE_THETA, **kw)
 
 
 def errors(got, ref):
@@ -75,3 +76,34 @@ def assert_close(got, ref, dtype, what):
 def say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def to_paged(kc, vc, lengths, bs, *, seed=0, spare=3):
+    """Scatter contiguous host caches [S, n_kv, cap, dh] into pools
+    [num_blocks, n_kv, bs, dh] under a random block table covering lengths[s]
+    (+ the slots the call writes); unused blocks hold NaN."""
+    S, n_kv, cap, dh = kc.shape
+    need = [(int(L) + bs - 1) // bs for L in lengths]
+    mb = max(max(need), 1)
+    nb = sum(need) + spare
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(nb)
+    table = np.zeros((S, mb), np.int32)
+    kp = np.full((nb, n_kv, bs, dh), np.nan, np.float32)
+    vp = np.full_like(kp, np.nan)
+    nxt = 0
+    for s in range(S):
+        for i in range(need[s]):
+            blk = int(perm[nxt]); nxt += 1
+            table[s, i] = blk
+            lo, hi = i * bs, min((i + 1) * bs, cap)
+            kp[blk, :, : hi - lo] = kc[s, :, lo:hi]
+            vp[blk, :, : hi - lo] = vc[s, :, lo:hi]
+        table[s, need[s]:] = table[s, max(need[s] - 1, 0)]   # never reached
+    return kp, vp, table
+
+
+def from_paged(pool, table, s, L):
+    bs = pool.shape[2]
+    rows = [pool[table[s, p // bs], :, p % bs] for p in range(L)]
+    return np.stack(rows, axis=1) if rows else np.zeros((pool.shape[1], 0, pool.shape[3]))

@@ -49,6 +49,7 @@ WEIGHTS = q3.Qwen3AttnWeights(*([0x1000] * 6))   # never dereferenced: validatio
     (dict(eps=float("nan")), 1),
     (dict(rope_theta=0.5), 1),
     (dict(rope_theta=float("inf")), 1),
+    (dict(sliding_window=-1), 1),
 ])
 def test_create_rejects_bad_descriptors_before_any_hip_call(built_lib, kw, status):
     st, h = q3.qwen3_attn_create(desc(**kw), WEIGHTS, 0)
@@ -104,6 +105,13 @@ def test_workspace_size_prefill_and_decode(built_lib):
 def test_workspace_size_zero_for_invalid(built_lib, args):
     assert q3.qwen3_attn_workspace_size(desc(), *args) == 0
     assert q3.qwen3_attn_workspace_size(desc(n_q=12), 0, 1, 8, 0) == 0
+    assert q3.qwen3_attn_workspace_size(desc(sliding_window=-4), 0, 1, 8, 0) == 0
+
+
+def test_sliding_window_leaves_the_workspace_unchanged(built_lib):
+    for args in ((0, 2, 2048, 0), (0, 1, 128, 0), (1, 64, 1, 32832)):
+        assert (q3.qwen3_attn_workspace_size(desc(sliding_window=4096), *args)
+                == q3.qwen3_attn_workspace_size(desc(), *args) > 0)
 
 
 def test_forward_with_null_handle_is_einval(built_lib):

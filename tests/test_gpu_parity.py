@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close, block_from_inputs, dev, host, say
+from gpu_util import assert_close, block_from_inputs, dev, from_paged, host, say, to_paged
 from workloads import (EPS, ROPE_THETA, WORKLOADS, decode_cache_host, decode_inputs,
                        prefill_inputs)
 
@@ -418,37 +418,6 @@ def test_layer_decode_parity(dtype, N):
 
 
 # --------------------------------------------------------------------- paged KV
-def to_paged(kc, vc, lengths, bs, *, seed=0, spare=3):
-    """Scatter contiguous host caches [S, n_kv, cap, dh] into pools
-    [num_blocks, n_kv, bs, dh] under a random block table covering lengths[s]
-    (+ the slots the call writes); unused blocks hold NaN."""
-    S, n_kv, cap, dh = kc.shape
-    need = [(int(L) + bs - 1) // bs for L in lengths]
-    mb = max(max(need), 1)
-    nb = sum(need) + spare
-    rng = np.random.default_rng(seed)
-    perm = rng.permutation(nb)
-    table = np.zeros((S, mb), np.int32)
-    kp = np.full((nb, n_kv, bs, dh), np.nan, np.float32)
-    vp = np.full_like(kp, np.nan)
-    nxt = 0
-    for s in range(S):
-        for i in range(need[s]):
-            blk = int(perm[nxt]); nxt += 1
-            table[s, i] = blk
-            lo, hi = i * bs, min((i + 1) * bs, cap)
-            kp[blk, :, : hi - lo] = kc[s, :, lo:hi]
-            vp[blk, :, : hi - lo] = vc[s, :, lo:hi]
-        table[s, need[s]:] = table[s, max(need[s] - 1, 0)]   # never reached
-    return kp, vp, table
-
-
-def from_paged(pool, table, s, L):
-    bs = pool.shape[2]
-    rows = [pool[table[s, p // bs], :, p % bs] for p in range(L)]
-    return np.stack(rows, axis=1) if rows else np.zeros((pool.shape[1], 0, pool.shape[3]))
-
-
 @pytest.mark.parametrize("dtype,bs", [("bf16", 64), ("bf16", 256), ("f32", 128)])
 def test_decode_paged_parity(dtype, bs):
     import torch
