@@ -206,6 +206,49 @@ qwen3_attn_status qwen3_attn_forward_prefill_paged(qwen3_attn_t* h, const void* 
                                                    void* workspace, size_t workspace_bytes,
                                                    void* stream);
 
+/* Variable-length batch: the tokens of B requests of different lengths packed
+ * into one token list, each request attending only to its own keys ("Assembling
+ * a large model from scratch", section "Inference view": the tokens of many
+ * requests form one batch with attention computed per request; the summary
+ * list after the section's opening: flattened tokens plus batching metadata).
+ *   hidden     [total_tokens, d_model], the requests one after another
+ *   positions  [total_tokens] int32, drives RoPE only
+ *   cu_seqlens [B + 1] int32 DEVICE array: request b owns token rows
+ *              cu_seqlens[b] .. cu_seqlens[b+1]-1.  Preconditions (not
+ *              checked, device data): cu_seqlens[0] = 0, non-decreasing,
+ *              cu_seqlens[B] = total_tokens, every length <= max_seqlen
+ *              (empty requests are allowed).
+ *   past_len   [B] int32 DEVICE array or NULL: tokens request b already
+ *              holds in its cache; its token t is written to slot
+ *              past_len[b] + t and sees slots 0 .. past_len[b] + t (as
+ *              qwen3_attn_forward_prefill_chunk).
+ *   block_table NULL: k_cache, v_cache are [B, n_kv, cache_cap, d_head]
+ *              (max_blocks and block_size unused); else they are pools
+ *              [num_blocks, n_kv, block_size, d_head] addressed through the
+ *              table [B, max_blocks] as qwen3_attn_forward_prefill_paged
+ *              (cache_cap unused).  Precondition: past_len[b] + length of b
+ *              <= the cache's slots per request.
+ *   out        [total_tokens, d_model]
+ *   max_seqlen the longest request (1 <= max_seqlen <= total_tokens); the
+ *              kernels are sized for it, so a far larger value only wastes
+ *              launches.
+ * With every length equal to T this is qwen3_attn_forward_prefill_chunk
+ * (or _paged) bit for bit.  EINVAL if cu_seqlens is NULL, if
+ * B * max_seqlen < total_tokens, or for the argument errors of those calls.
+ * Workspace: qwen3_attn_workspace_size_varlen(desc, B, total_tokens,
+ * max_seqlen); layout as qwen3_attn_forward_prefill with total_tokens rows. */
+qwen3_attn_status qwen3_attn_forward_prefill_varlen(
+    qwen3_attn_t* h, const void* hidden, const int32_t* positions, const int32_t* cu_seqlens,
+    const int32_t* past_len, const int32_t* block_table, int32_t max_blocks, void* k_cache,
+    void* v_cache, int64_t cache_cap, int32_t block_size, void* out, int32_t B,
+    int32_t total_tokens, int32_t max_seqlen, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Workspace bytes of qwen3_attn_forward_prefill_varlen (0 if invalid).  Pure
+ * host computation. */
+size_t qwen3_attn_workspace_size_varlen(const qwen3_attn_desc* desc, int32_t B,
+                                        int32_t total_tokens, int32_t max_seqlen);
+
 /* Decode over a paged cache: as qwen3_attn_forward_decode (positions[s] =
  * L_s cached tokens; the new token is written at position L_s and attends to
  * positions 0..L_s), with the rows found through the block table.

@@ -22,6 +22,7 @@ STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EWORKSPACE",
 EXPORTED = ("qwen3_attn_create", "qwen3_attn_create_with_input_norm", "qwen3_attn_workspace_size",
             "qwen3_attn_forward_prefill",
             "qwen3_attn_forward_prefill_chunk", "qwen3_attn_forward_prefill_paged",
+            "qwen3_attn_forward_prefill_varlen", "qwen3_attn_workspace_size_varlen",
             "qwen3_attn_forward_decode", "qwen3_attn_forward_decode_paged", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
             "qwen3_attn_stage_times", "qwen3_attn_status_string")
 STAGES = ("qkv_norm_rope_gemm", "attention", "o_proj_gemm")
@@ -74,6 +75,11 @@ def lib() -> ctypes.CDLL:
         L.qwen3_attn_forward_prefill_paged.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, i32,
                                                        i32, vp, sz, vp]
         L.qwen3_attn_forward_prefill_paged.restype = ctypes.c_int
+        L.qwen3_attn_forward_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64,
+                                                        i32, vp, i32, i32, i32, vp, sz, vp]
+        L.qwen3_attn_forward_prefill_varlen.restype = ctypes.c_int
+        L.qwen3_attn_workspace_size_varlen.argtypes = [ctypes.POINTER(Qwen3AttnDesc), i32, i32, i32]
+        L.qwen3_attn_workspace_size_varlen.restype = sz
         L.qwen3_attn_forward_decode_paged.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, vp, i32, vp,
                                                       sz, vp]
         L.qwen3_attn_forward_decode_paged.restype = ctypes.c_int
@@ -138,6 +144,21 @@ def qwen3_attn_forward_prefill_paged(handle, hidden, positions, past_len, block_
     return lib().qwen3_attn_forward_prefill_paged(handle, hidden, positions, past_len, block_table,
                                                   max_blocks, k_pool, v_pool, block_size, out, B, T,
                                                   workspace, workspace_bytes, stream)
+
+
+def qwen3_attn_forward_prefill_varlen(handle, hidden, positions, cu_seqlens, past_len, block_table,
+                                      max_blocks, k_cache, v_cache, cache_cap, block_size, out, B,
+                                      total_tokens, max_seqlen, workspace, workspace_bytes,
+                                      stream) -> int:
+    return lib().qwen3_attn_forward_prefill_varlen(handle, hidden, positions, cu_seqlens, past_len,
+                                                   block_table, max_blocks, k_cache, v_cache,
+                                                   cache_cap, block_size, out, B, total_tokens,
+                                                   max_seqlen, workspace, workspace_bytes, stream)
+
+
+def qwen3_attn_workspace_size_varlen(desc: Qwen3AttnDesc, B: int, total_tokens: int,
+                                     max_seqlen: int) -> int:
+    return lib().qwen3_attn_workspace_size_varlen(ctypes.byref(desc), B, total_tokens, max_seqlen)
 
 
 def qwen3_attn_forward_decode_paged(handle, hidden, positions, block_table, max_blocks, k_pool,
@@ -328,6 +349,37 @@ class Qwen3Attention:
             ws.numel() * ws.element_size(), torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise Qwen3AttnError("qwen3_attn_forward_prefill_paged", st)
+        return out
+
+    def prefill_varlen(self, hidden, positions, cu_seqlens, k_cache, v_cache, *, max_seqlen,
+                       past_len=None, block_table=None, out=None, workspace=None):
+        """A variable-length batch: hidden [total, d] holds the requests one after
+        another, cu_seqlens [B+1] int32 (device) their row offsets.  block_table
+        None: caches [B, n_kv, cap, 128]; else pools [num_blocks, n_kv, block_size,
+        128] with block_table [B, max_blocks]."""
+        torch = _torch()
+        total, d = hidden.shape
+        B = cu_seqlens.shape[0] - 1
+        if out is None:
+            out = torch.empty_like(hidden)
+        ws = self._workspace(qwen3_attn_workspace_size_varlen(self.desc, B, total, max_seqlen),
+                             workspace)
+        n0, _, s2, _ = k_cache.shape
+        kshape = (n0, self.n_kv, s2, self.d_head)
+        mb = 0 if block_table is None else block_table.shape[1]
+        st = qwen3_attn_forward_prefill_varlen(
+            self.handle, _ptr(hidden, "hidden", self.dtype),
+            _ptr(positions, "positions", torch.int32, (total,)),
+            _ptr(cu_seqlens, "cu_seqlens", torch.int32, (B + 1,)),
+            None if past_len is None else _ptr(past_len, "past_len", torch.int32, (B,)),
+            None if block_table is None else _ptr(block_table, "block_table", torch.int32, (B, mb)),
+            mb, _ptr(k_cache, "k_cache", self.dtype, kshape),
+            _ptr(v_cache, "v_cache", self.dtype, kshape),
+            s2 if block_table is None else 0, 0 if block_table is None else s2,
+            _ptr(out, "out", self.dtype, (total, d)), B, total, max_seqlen, _ptr(ws, "workspace"),
+            ws.numel() * ws.element_size(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise Qwen3AttnError("qwen3_attn_forward_prefill_varlen", st)
         return out
 
     def decode_paged(self, hidden, positions, block_table, k_pool, v_pool, out=None,

@@ -57,6 +57,27 @@ struct WsLayout {
   bool part;  // decode projections run split-K through the part region
 };
 
+// Prefill of B sequences with n_tok token rows in all, at most max_T each.
+bool ws_layout_prefill(const qwen3_attn_desc* d, int32_t B, int32_t n_tok, int32_t max_T,
+                       WsLayout* L) {
+  if (check_desc(d) != QWEN3_ATTN_OK) return false;
+  if (B <= 0 || n_tok <= 0 || max_T <= 0 || max_T > n_tok) return false;
+  if (n_tok > INT_MAX / 2 || (int64_t)B * max_T > INT_MAX / 2) return false;
+  const size_t es = elem_size(d->dtype);
+  const size_t hq = (size_t)d->n_q * 128;
+  const size_t qb = align_up((size_t)n_tok * hq * es);
+  L->q_off = 0;
+  L->a_off = qb;
+  L->cs_off = 2 * qb;
+  L->acc_off = L->ml_off = 0;
+  L->nchunk = 0;
+  L->part = false;
+  L->part_off = L->cs_off + align_up((size_t)n_tok * 64 * 2 * sizeof(float));
+  L->total = L->part_off +
+             align_up(q3::flash_partial_floats(B, max_T, d->n_q, d->n_kv, n_tok) * sizeof(float));
+  return true;
+}
+
 bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, int64_t cap,
                WsLayout* L) {
   if (check_desc(d) != QWEN3_ATTN_OK) return false;
@@ -65,17 +86,7 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
   const size_t hq = (size_t)d->n_q * 128;
   if (!is_decode) {
     if ((int64_t)n * T > INT_MAX / 2) return false;
-    const size_t qb = align_up((size_t)n * T * hq * es);
-    L->q_off = 0;
-    L->a_off = qb;
-    L->cs_off = 2 * qb;
-    L->acc_off = L->ml_off = 0;
-    L->nchunk = 0;
-    L->part = false;
-    L->part_off = L->cs_off + align_up((size_t)n * T * 64 * 2 * sizeof(float));
-    L->total = L->part_off +
-               align_up(q3::flash_partial_floats(n, T, d->n_q, d->n_kv) * sizeof(float));
-    return true;
+    return ws_layout_prefill(d, n, n * T, T, L);
   }
   if (T != 1 || cap <= 0 || cap > INT_MAX) return false;
   const int chunk = q3::decode_chunk_keys();
@@ -132,11 +143,11 @@ qwen3_attn_status hip_status(hipError_t e) {
 
 template <typename T>
 qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
-                              const int32_t* past, void* k_cache, void* v_cache,
-                              const q3::KvAddr& kv, void* out, int B, int T_len, char* ws,
-                              const WsLayout& L, hipStream_t s) {
+                              const int32_t* past, const int32_t* cu_seqlens, void* k_cache,
+                              void* v_cache, const q3::KvAddr& kv, void* out, int B, int T_len,
+                              int n_tok, char* ws, const WsLayout& L, hipStream_t s) {
   const qwen3_attn_desc& d = h->desc;
-  const int M = B * T_len;
+  const int M = n_tok;
   const int nqkv = (d.n_q + 2 * d.n_kv) * 128;
   const int hq = d.n_q * 128;
   T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
@@ -144,7 +155,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
                     d.n_q, d.n_kv, kv, T_len, 0, d.eps, past,
-                    h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2};
+                    h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2, cu_seqlens, B};
   mark(h, s, 0);
   hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, M, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
@@ -154,8 +165,8 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 1);
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
-                                  reinterpret_cast<const T*>(v_cache), abuf, B, T_len, d.n_q, d.n_kv,
-                                  kv, past, d.sliding_window,
+                                  reinterpret_cast<const T*>(v_cache), abuf, B, T_len, cu_seqlens,
+                                  n_tok, d.n_q, d.n_kv, kv, past, d.sliding_window,
                                   reinterpret_cast<float*>(ws + L.part_off), s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
@@ -311,6 +322,14 @@ size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
   return L.total;
 }
 
+size_t qwen3_attn_workspace_size_varlen(const qwen3_attn_desc* desc, int32_t B,
+                                        int32_t total_tokens, int32_t max_seqlen) {
+  WsLayout L;
+  if ((int64_t)B * max_seqlen < total_tokens) return 0;
+  if (!ws_layout_prefill(desc, B, total_tokens, max_seqlen, &L)) return 0;
+  return L.total;
+}
+
 namespace {
 // Paged cache addressing from the caller's block size (0 if unsupported).
 bool paged_addr(const qwen3_attn_desc& d, const int32_t* table, int32_t max_blocks,
@@ -325,27 +344,30 @@ bool paged_addr(const qwen3_attn_desc& d, const int32_t* table, int32_t max_bloc
   return true;
 }
 
+// T is the chunk length of every sequence, or with cu_seqlens the longest
+// one of a variable-length batch of n_tok rows in all (else n_tok = B * T).
 qwen3_attn_status prefill_entry(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
-                                const int32_t* past, void* k_cache, void* v_cache,
-                                const q3::KvAddr* paged, int64_t cache_cap, void* out, int32_t B,
-                                int32_t T, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                const int32_t* past, const int32_t* cu_seqlens, void* k_cache,
+                                void* v_cache, const q3::KvAddr* paged, int64_t cache_cap,
+                                void* out, int32_t B, int32_t T, int32_t n_tok, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   if (!h || !hidden || !positions || !k_cache || !v_cache || !out) return QWEN3_ATTN_EINVAL;
-  if (B <= 0 || T <= 0 || cache_cap <= 0 || T > cache_cap) return QWEN3_ATTN_EINVAL;
+  if (B <= 0 || T <= 0 || n_tok <= 0 || cache_cap <= 0 || T > cache_cap) return QWEN3_ATTN_EINVAL;
+  if (cu_seqlens ? T > n_tok : (int64_t)B * T != n_tok) return QWEN3_ATTN_EINVAL;
   if (B > 65535 || cache_cap > INT_MAX) return QWEN3_ATTN_EUNSUPPORTED;
   const q3::KvAddr kv = paged ? *paged : q3::KvAddr{nullptr, cache_cap, 0, 0, h->desc.n_kv};
   WsLayout L;
-  if (!ws_layout(&h->desc, 0, B, T, cache_cap, &L)) return QWEN3_ATTN_EUNSUPPORTED;
+  if (!ws_layout_prefill(&h->desc, B, n_tok, T, &L)) return QWEN3_ATTN_EUNSUPPORTED;
   if (!workspace || workspace_bytes < L.total) return QWEN3_ATTN_EWORKSPACE;
   qwen3_attn_status st = check_handle_device(h);
   if (st != QWEN3_ATTN_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (h->desc.dtype == QWEN3_ATTN_F32)
-    return run_prefill<float>(h, hidden, positions, past, k_cache, v_cache, kv, out, B, T, ws, L,
-                              s);
-  return run_prefill<q3::bf16_t>(h, hidden, positions, past, k_cache, v_cache, kv, out, B, T, ws,
-                                 L, s);
+    return run_prefill<float>(h, hidden, positions, past, cu_seqlens, k_cache, v_cache, kv, out,
+                              B, T, n_tok, ws, L, s);
+  return run_prefill<q3::bf16_t>(h, hidden, positions, past, cu_seqlens, k_cache, v_cache, kv,
+                                 out, B, T, n_tok, ws, L, s);
 }
 
 qwen3_attn_status decode_entry(qwen3_attn_t* h, const void* hidden, const int32_t* positions,
@@ -375,8 +397,8 @@ qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden
                                              void* v_cache, int64_t cache_cap, void* out,
                                              int32_t B, int32_t T, void* workspace,
                                              size_t workspace_bytes, void* stream) {
-  return prefill_entry(h, hidden, positions, nullptr, k_cache, v_cache, nullptr, cache_cap, out,
-                       B, T, workspace, workspace_bytes, stream);
+  return prefill_entry(h, hidden, positions, nullptr, nullptr, k_cache, v_cache, nullptr,
+                       cache_cap, out, B, T, B * T, workspace, workspace_bytes, stream);
 }
 
 qwen3_attn_status qwen3_attn_forward_prefill_chunk(qwen3_attn_t* h, const void* hidden,
@@ -386,8 +408,8 @@ qwen3_attn_status qwen3_attn_forward_prefill_chunk(qwen3_attn_t* h, const void* 
                                                    int32_t B, int32_t T, void* workspace,
                                                    size_t workspace_bytes, void* stream) {
   if (!past_len) return QWEN3_ATTN_EINVAL;
-  return prefill_entry(h, hidden, positions, past_len, k_cache, v_cache, nullptr, cache_cap, out,
-                       B, T, workspace, workspace_bytes, stream);
+  return prefill_entry(h, hidden, positions, past_len, nullptr, k_cache, v_cache, nullptr,
+                       cache_cap, out, B, T, B * T, workspace, workspace_bytes, stream);
 }
 
 qwen3_attn_status qwen3_attn_forward_prefill_paged(qwen3_attn_t* h, const void* hidden,
@@ -401,9 +423,28 @@ qwen3_attn_status qwen3_attn_forward_prefill_paged(qwen3_attn_t* h, const void* 
   if (!h) return QWEN3_ATTN_EINVAL;
   q3::KvAddr kv;
   if (!paged_addr(h->desc, block_table, max_blocks, block_size, &kv)) return QWEN3_ATTN_EINVAL;
-  return prefill_entry(h, hidden, positions, past_len, k_pool, v_pool, &kv,
-                       (int64_t)max_blocks * block_size, out, B, T, workspace, workspace_bytes,
-                       stream);
+  return prefill_entry(h, hidden, positions, past_len, nullptr, k_pool, v_pool, &kv,
+                       (int64_t)max_blocks * block_size, out, B, T, B * T, workspace,
+                       workspace_bytes, stream);
+}
+
+qwen3_attn_status qwen3_attn_forward_prefill_varlen(
+    qwen3_attn_t* h, const void* hidden, const int32_t* positions, const int32_t* cu_seqlens,
+    const int32_t* past_len, const int32_t* block_table, int32_t max_blocks, void* k_cache,
+    void* v_cache, int64_t cache_cap, int32_t block_size, void* out, int32_t B,
+    int32_t total_tokens, int32_t max_seqlen, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (!h || !cu_seqlens) return QWEN3_ATTN_EINVAL;
+  if ((int64_t)B * max_seqlen < total_tokens) return QWEN3_ATTN_EINVAL;
+  if (!block_table)
+    return prefill_entry(h, hidden, positions, past_len, cu_seqlens, k_cache, v_cache, nullptr,
+                         cache_cap, out, B, max_seqlen, total_tokens, workspace, workspace_bytes,
+                         stream);
+  q3::KvAddr kv;
+  if (!paged_addr(h->desc, block_table, max_blocks, block_size, &kv)) return QWEN3_ATTN_EINVAL;
+  return prefill_entry(h, hidden, positions, past_len, cu_seqlens, k_cache, v_cache, &kv,
+                       (int64_t)max_blocks * block_size, out, B, max_seqlen, total_tokens,
+                       workspace, workspace_bytes, stream);
 }
 
 qwen3_attn_status qwen3_attn_forward_decode_paged(qwen3_attn_t* h, const void* hidden,

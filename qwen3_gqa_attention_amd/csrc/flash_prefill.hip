@@ -56,6 +56,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc,
                                                             T* __restrict__ Out, int B, int T_len,
+                                                            const int32_t* __restrict__ cu_seqlens,
+                                                            int n_tok,
                                                             int n_q, int n_kv, KvAddr kv,
                                                             const int32_t* __restrict__ past,
                                                             int window, int nsplit,
@@ -84,8 +86,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   auto Vs = [&](int st) { return smem + 2 * KSPLIT * KSZ + st * VSZ; };
 
   const int n_rep = n_q / n_kv;
-  const int rows_total = T_len * n_rep;
-  const int tiles_per_group = (rows_total + 127) / 128;
+  // T_len is the (longest) chunk length the grid was sized for.
+  const int tiles_per_group = (T_len * n_rep + 127) / 128;
   const int groups = B * n_kv;
   // With nsplit > 1 the key range of each query tile is cut into nsplit
   // parts run by separate workgroups (few query tiles: fill the chip); each
@@ -100,10 +102,17 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // ones fill CUs as they free up.
   const int qt = tiles_per_group - 1 - rest / nsplit;
   const int b = bg / n_kv, g = bg % n_kv;
+  // Token rows of sequence b: q0 .. q0 + Tb - 1 (a variable-length batch
+  // gives them in cu_seqlens; else every sequence has T_len).  Query tiles
+  // past a shorter sequence's end have no work.
+  const int q0 = cu_seqlens ? cu_seqlens[b] : b * T_len;
+  const int Tb = cu_seqlens ? cu_seqlens[b + 1] - q0 : T_len;
+  const int rows_total = Tb * n_rep;
+  if (qt * 128 >= rows_total) return;  // whole workgroup, before any barrier
   // Chunked prefill: the sequence already holds P cached tokens, chunk token
   // t is key P + t and sees keys 0 .. P + t (P = 0 for a first prefill).
   const int P = past ? past[b] : 0;
-  const int S_len = P + T_len;
+  const int S_len = P + Tb;
 
   // Wave w owns query block w & 3 (32 rows) over key half w >> 2 (with
   // KSPLIT = 2; with KSPLIT = 1 four waves cover the whole key range).
@@ -117,7 +126,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int Rw = R0 + qblk * 32;
   const int Rl = Rw + c32;
   const bool row_ok = Rl < rows_total;
-  const int qtok = row_ok ? Rl / n_rep : T_len - 1;   // token inside the chunk
+  const int qtok = row_ok ? Rl / n_rep : Tb - 1;      // token inside the chunk
   const int tok = P + qtok;                            // its key position
   const int head = g * n_rep + (row_ok ? Rl % n_rep : 0);
   const bool wave_active = Rw < rows_total;
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // Q^T fragments for the whole d_head, kept in VGPRs.
   typename MF::frag qf[DSTEPS];
   {
-    const T* qrow = Q + ((size_t)(b * T_len + qtok) * n_q + head) * kHeadDim + hk * MF::KL;
+    const T* qrow = Q + ((size_t)(q0 + qtok) * n_q + head) * kHeadDim + hk * MF::KL;
 #pragma unroll
     for (int ks = 0; ks < DSTEPS; ++ks) qf[ks] = row_ok ? MF::load(qrow + ks * MF::K) : MF::zero();
   }
@@ -454,7 +463,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   l_run += __shfl_xor(l_run, 32, kWave);
   if (nsplit > 1) {
     // Partial results of this key range: O unnormalised, and (m, l).
-    const size_t prow = ((size_t)split * B * T_len + (size_t)b * T_len + qtok) * n_q + head;
+    const size_t prow = ((size_t)split * n_tok + q0 + qtok) * n_q + head;
     float* po = part + prow * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -465,14 +474,14 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
             f32x4_v{o[db][i4 * 4 + 0], o[db][i4 * 4 + 1], o[db][i4 * 4 + 2], o[db][i4 * 4 + 3]};
       }
     if (hk == 0) {
-      float* pml = part + (size_t)nsplit * B * T_len * n_q * kHeadDim + prow * 2;
+      float* pml = part + (size_t)nsplit * n_tok * n_q * kHeadDim + prow * 2;
       pml[0] = m_run;
       pml[1] = l_run;
     }
     return;
   }
   const float inv = 1.f / l_run;
-  T* orow = Out + ((size_t)(b * T_len + qtok) * n_q + head) * kHeadDim;
+  T* orow = Out + ((size_t)(q0 + qtok) * n_q + head) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -532,15 +541,16 @@ int flash_splits(int B, int T_len, int n_q, int n_kv) {
   const int sp = 256 / wgs;
   return sp < 2 ? 2 : (sp > 8 ? 8 : sp);
 }
-size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv) {
+size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv, int n_tok) {
   const int sp = flash_splits(B, T_len, n_q, n_kv);
-  return sp > 1 ? (size_t)sp * B * T_len * n_q * (kHeadDim + 2) : 0;
+  return sp > 1 ? (size_t)sp * n_tok * n_q * (kHeadDim + 2) : 0;
 }
 
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
-                                int n_q, int n_kv, const KvAddr& kv, const int32_t* past,
-                                int window, float* part, hipStream_t s) {
+                                const int32_t* cu_seqlens, int n_tok, int n_q, int n_kv,
+                                const KvAddr& kv, const int32_t* past, int window, float* part,
+                                hipStream_t s) {
   if (window < 0) return hipErrorInvalidValue;
   const int nsplit = flash_splits(B, T_len, n_q, n_kv);
   if (nsplit > 1 && !part) return hipErrorInvalidValue;
@@ -550,14 +560,14 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
   const int wgs = flash_query_wgs(B, T_len, n_q, n_kv) * nsplit;
   if (wgs < 4 * 256)
     hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, kv, past, window, nsplit, part);
+                       T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part);
   else
     hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, n_q, n_kv, kv, past, window, nsplit, part);
+                       T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part);
   if (nsplit > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int pairs = B * T_len * n_q;
+    const int pairs = n_tok * n_q;
     hipLaunchKernelGGL(flash_combine_kernel<T>, dim3((pairs + 7) / 8), dim3(256), 0, s, part,
                        nsplit, pairs, Out);
   }
@@ -565,10 +575,12 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
 }
 
 template hipError_t launch_flash_prefill<float>(const float*, const float*, const float*, float*,
-                                                int, int, int, int, const KvAddr&,
-                                                const int32_t*, int, float*, hipStream_t);
+                                                int, int, const int32_t*, int, int, int,
+                                                const KvAddr&, const int32_t*, int, float*,
+                                                hipStream_t);
 template hipError_t launch_flash_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
-                                                 bf16_t*, int, int, int, int, const KvAddr&,
-                                                 const int32_t*, int, float*, hipStream_t);
+                                                 bf16_t*, int, int, const int32_t*, int, int, int,
+                                                 const KvAddr&, const int32_t*, int, float*,
+                                                 hipStream_t);
 
 }  // namespace q3

@@ -366,9 +366,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
       if (kind == 0)
         return reinterpret_cast<T*>(qe.q_out) + (size_t)row * (qe.n_q * kHeadDim) + head * kHeadDim;
       const int g = head - qe.n_q - (kind == 2 ? qe.n_kv : 0);
-      const int seq = qe.decode ? row : row / qe.rows_per_seq;
-      const int slot = qe.decode ? qe.positions[row]
-                                 : row % qe.rows_per_seq + (qe.past ? qe.past[seq] : 0);
+      int seq, slot;
+      qe.seq_slot(row, &seq, &slot);
       T* cache = reinterpret_cast<T*>(kind == 1 ? qe.k_cache : qe.v_cache);
       return cache + qe.kv.row(seq, g, slot) * kHeadDim;
     }
@@ -521,9 +520,8 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
     dst = reinterpret_cast<T*>(qe.q_out) + (size_t)row * (qe.n_q * kHeadDim) + head * kHeadDim;
   } else {
     const int g = head - qe.n_q - (kind == 2 ? qe.n_kv : 0);
-    const int seq = qe.decode ? row : row / qe.rows_per_seq;
-    const int slot = qe.decode ? qe.positions[row]
-                               : row % qe.rows_per_seq + (qe.past ? qe.past[seq] : 0);
+    int seq, slot;
+    qe.seq_slot(row, &seq, &slot);
     T* cache = reinterpret_cast<T*>(kind == 1 ? qe.k_cache : qe.v_cache);
     dst = cache + qe.kv.row(seq, g, slot) * kHeadDim;
   }

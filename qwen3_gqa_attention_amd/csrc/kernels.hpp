@@ -53,6 +53,36 @@ struct QkvEpilogue {
                              // the weights); x [rows, d] is read to form 1/rms per row
   float q_scale;             // q~ is stored times this (log2(e) / sqrt(d_head): the
                              // attention kernels then take exp2 of raw dot products)
+  const int32_t* cu_seqlens; // prefill of a variable-length batch: [nseq + 1] row offsets,
+                             // sequence s owns rows cu[s] .. cu[s+1]-1 (slot = past[s] +
+                             // row - cu[s]); null: rows_per_seq rows each
+  int nseq;
+
+  // Sequence and cache slot of projection row `row` (prefill and decode).
+  __device__ __forceinline__ void seq_slot(int row, int* seq, int* slot) const {
+    if (decode) {
+      *seq = row;
+      *slot = positions[row];
+      return;
+    }
+    int s, t;
+    if (cu_seqlens) {
+      // the last sequence whose first row is <= row (empty sequences skipped)
+      int lo = 0, hi = nseq - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_seqlens[mid] <= row) lo = mid;
+        else hi = mid - 1;
+      }
+      s = lo;
+      t = row - cu_seqlens[lo];
+    } else {
+      s = row / rows_per_seq;
+      t = row % rows_per_seq;
+    }
+    *seq = s;
+    *slot = t + (past ? past[s] : 0);
+  }
 };
 
 // cs[row][i] = (cos, sin)(positions[row] * omega_i), i < 64, with omega_i / (2 pi)
@@ -85,17 +115,21 @@ int small_m_partial_floats(int M, int N, int K, int elem_size);
 
 // Causal GQA flash attention of a T_len-token chunk over the caches, which
 // hold past[b] earlier tokens of sequence b followed by the chunk (past may
-// be null: empty caches).  window > 0 limits each token to the `window`
+// be null: empty caches).  cu_seqlens (may be null): a variable-length
+// batch, sequence b owning token rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of
+// the n_tok rows, at most T_len of them; null: every sequence has T_len
+// tokens (n_tok = B * T_len).  window > 0 limits each token to the `window`
 // most recent keys, its own included (0: full causal attention).
 // `part`: fp32 scratch of flash_partial_floats(...) floats (may be null when
 // that is 0): with few query tiles the key ranges are split over more
 // workgroups and merged by a second kernel.
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
-                                int n_q, int n_kv, const KvAddr& kv, const int32_t* past,
-                                int window, float* part, hipStream_t s);
+                                const int32_t* cu_seqlens, int n_tok, int n_q, int n_kv,
+                                const KvAddr& kv, const int32_t* past, int window, float* part,
+                                hipStream_t s);
 int flash_splits(int B, int T_len, int n_q, int n_kv);
-size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv);
+size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv, int n_tok);
 
 // Split-K decode attention: partial (max, sum, weighted values) per key chunk,
 // then the log-sum-exp merge into Out [N, n_q*128].  window > 0: the new

@@ -108,10 +108,32 @@ def test_workspace_size_zero_for_invalid(built_lib, args):
     assert q3.qwen3_attn_workspace_size(desc(sliding_window=-4), 0, 1, 8, 0) == 0
 
 
+def test_varlen_workspace_size(built_lib):
+    d = desc()
+    # equal lengths: the fixed-length prefill's workspace
+    for B, T in ((2, 2048), (1, 128), (3, 77)):
+        assert (q3.qwen3_attn_workspace_size_varlen(d, B, B * T, T)
+                == q3.qwen3_attn_workspace_size(d, 0, B, T, 0) > 0)
+    # ragged: rows sized by the total, key splits by B and the longest request
+    assert q3.qwen3_attn_workspace_size_varlen(d, 4, 1000, 700) > 0
+    for args in ((0, 10, 5), (2, 0, 1), (2, 10, 0), (2, 10, 11), (2, 10, 4)):
+        assert q3.qwen3_attn_workspace_size_varlen(d, *args) == 0, args
+
+
 def test_sliding_window_leaves_the_workspace_unchanged(built_lib):
     for args in ((0, 2, 2048, 0), (0, 1, 128, 0), (1, 64, 1, 32832)):
         assert (q3.qwen3_attn_workspace_size(desc(sliding_window=4096), *args)
                 == q3.qwen3_attn_workspace_size(desc(), *args) > 0)
+
+
+def test_varlen_rejects_missing_offsets_and_inconsistent_sizes(built_lib):
+    # cu_seqlens NULL, then B * max_seqlen < total: EINVAL before the handle is used
+    assert q3.qwen3_attn_forward_prefill_varlen(1, 1, 1, None, None, None, 0, 1, 1, 64, 0, 1, 2,
+                                                10, 5, 1, 1 << 20, None) == 1
+    assert q3.qwen3_attn_forward_prefill_varlen(1, 1, 1, 1, None, None, 0, 1, 1, 64, 0, 1, 2,
+                                                10, 4, 1, 1 << 20, None) == 1
+    assert q3.qwen3_attn_forward_prefill_varlen(None, 1, 1, 1, None, None, 0, 1, 1, 64, 0, 1, 2,
+                                                10, 5, 1, 1 << 20, None) == 1
 
 
 def test_forward_with_null_handle_is_einval(built_lib):
