@@ -141,16 +141,18 @@ def prefill_flops(B, T, d, n_q, n_kv, dh=128):
     }
 
 
-def bench_prefill(args, layer=False):
-    """The 0.6B-shaped prefill; with layer=True the block carries the fused
-    input RMSNorm and residual add (the attention half of a decoder layer)."""
+def bench_prefill(args, layer=False, idx=2, steps=None):
+    """The prefill of workload idx (default: the 0.6B shape, B=2, T=2048); with
+    layer=True the block carries the fused input RMSNorm and residual add (the
+    attention half of a decoder layer)."""
     import numpy as np
     import torch
 
     import qwen3_gqa_attention_amd as q3
     from workloads import EPS, ROPE_THETA, WORKLOADS, prefill_inputs
 
-    w = WORKLOADS[2]
+    steps = steps or args.steps
+    w = WORKLOADS[idx]
     B, T = w.B, w.T
     inp = prefill_inputs(w)
     bf = torch.bfloat16
@@ -174,7 +176,7 @@ def bench_prefill(args, layer=False):
 
     # timed region 1: K plain steps -> the reported throughput
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         blk.prefill(x, pos, kc, vc, out=out, workspace=ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -182,18 +184,18 @@ def bench_prefill(args, layer=False):
     # between its kernels, on the stream it launches on -> per-kernel
     # durations (the events add a few microseconds per step, so this pass is
     # not the one `value` comes from)
-    blk.enable_stage_timing(args.steps)
+    blk.enable_stage_timing(steps)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         blk.prefill(x, pos, kc, vc, out=out, workspace=ws)
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     stage_ms, ncalls = blk.stage_times()
     blk.enable_stage_timing(0)
 
-    step_s = (t1 - t0) / args.steps
-    step_events_s = (t3 - t2) / args.steps
+    step_s = (t1 - t0) / steps
+    step_events_s = (t3 - t2) / steps
     flops = prefill_flops(B, T, w.d, w.n_q, w.n_kv)
     kernels = {}
     for name, tot in zip(q3.STAGES, stage_ms):
@@ -388,6 +390,51 @@ def bench_decode_paged(args, bs=64):
             "GBps": nbytes / step_s / 1e9, "frac_hbm_peak": nbytes / step_s / PEAK_HBM_BYTES}
 
 
+def bench_prefill_cold(args, calls=50, flush_mb=512):
+    """Per-call HIP-event times of the 0.6B-shaped prefill, hot (back to back)
+    and cold (a 512 MB buffer rewritten before each call evicts the block's
+    ~80 MB working set from L2 and the Infinity Cache); median and minimum."""
+    import numpy as np
+    import torch
+
+    import qwen3_gqa_attention_amd as q3
+    from workloads import EPS, ROPE_THETA, WORKLOADS, prefill_inputs
+
+    w = WORKLOADS[2]
+    B, T = w.B, w.T
+    inp = prefill_inputs(w)
+    bf = torch.bfloat16
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(bf)
+    blk = q3.Qwen3Attention(d(inp["Wq"]), d(inp["Wk"]), d(inp["Wv"]), d(inp["Wo"]), d(inp["gq"]),
+                            d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA)
+    x = d(inp["X"])
+    pos = torch.from_numpy(inp["positions"]).cuda()
+    kc = torch.empty((B, w.n_kv, T, 128), dtype=bf, device="cuda")
+    vc = torch.empty_like(kc)
+    out = torch.empty_like(x)
+    ws = torch.empty(blk.workspace_size(False, B, T), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda")
+    res = {}
+    for mode in ("hot", "cold"):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls)]
+        for _ in range(5):
+            blk.prefill(x, pos, kc, vc, out=out, workspace=ws)
+        for e0, e1 in ev:
+            if mode == "cold":
+                flush.fill_(1)
+            e0.record()
+            blk.prefill(x, pos, kc, vc, out=out, workspace=ws)
+            e1.record()
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        res[mode] = {"median_ms": ms[len(ms) // 2], "min_ms": ms[0]}
+    blk.close()
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(seconds):
     """The fp64 oracle's own code run in float32 on host cores, bounded sample."""
     import numpy as np
@@ -423,6 +470,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="run only the prefill step and the full-attention decode (the two "
+                         "roofline kernels), e.g. under a profiler")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy of known size (for PMC traffic calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -453,18 +503,38 @@ def main():
     p = bench_prefill(args)
     log(f"bench: prefill {p['step_s'] * 1e3:.4f} ms/step; kernels " +
         ", ".join(f"{k} {v['avg_ms']:.4f} ms" for k, v in p["kernels"].items()))
-    log("bench: the same prefill with the fused input RMSNorm + residual add")
-    pl = bench_prefill(args, layer=True)
-    layer = {"workload": f"{pl['w'].name}-input-norm-residual",
-             "ms_per_step": pl["step_s"] * 1e3, "tokens_per_s": pl["B"] * pl["T"] / pl["step_s"],
-             "overhead_vs_block": pl["step_s"] / p["step_s"] - 1.0,
-             "kernel_ms": {k: v["avg_ms"] for k, v in pl["kernels"].items()}}
-    log(f"bench: layer prefill {layer['ms_per_step']:.4f} ms/step "
-        f"({layer['overhead_vs_block'] * 100:+.1f}% vs the block alone)")
-    log("bench: chunked prefill 0.6B-shape B=2, 512 tokens over 1536 cached")
-    chunk = bench_chunk(args)
-    log(f"bench: chunked prefill {chunk['ms_per_step']:.4f} ms/step, "
-        f"{chunk['frac_mfma_peak'] * 100:.1f}% of MFMA peak")
+    layer = chunk = dec_window = dec_paged = cold = None
+    other = {}
+    extras = not args.headline_only
+    if extras:
+        log("bench: the same prefill with the fused input RMSNorm + residual add")
+        pl = bench_prefill(args, layer=True)
+        layer = {"workload": f"{pl['w'].name}-input-norm-residual",
+                 "ms_per_step": pl["step_s"] * 1e3,
+                 "tokens_per_s": pl["B"] * pl["T"] / pl["step_s"],
+                 "overhead_vs_block": pl["step_s"] / p["step_s"] - 1.0,
+                 "kernel_ms": {k: v["avg_ms"] for k, v in pl["kernels"].items()}}
+        log(f"bench: layer prefill {layer['ms_per_step']:.4f} ms/step "
+            f"({layer['overhead_vs_block'] * 100:+.1f}% vs the block alone)")
+        log("bench: prefill per-call times, hot and with the caches flushed")
+        cold = bench_prefill_cold(args)
+        log(f"bench: prefill per call: hot median {cold['hot']['median_ms']:.4f} ms, "
+            f"cold median {cold['cold']['median_ms']:.4f} ms")
+        for idx in (3, 4):
+            pc = bench_prefill(args, idx=idx, steps=max(args.steps // (4 if idx == 3 else 20), 5))
+            wc = pc["w"]
+            other[wc.name] = {
+                "B": pc["B"], "T": pc["T"], "ms_per_step": pc["step_s"] * 1e3,
+                "tokens_per_s": pc["B"] * pc["T"] / pc["step_s"],
+                "tflops": pc["total_flops"] / pc["step_s"] / 1e12,
+                "frac_mfma_peak": pc["total_flops"] / pc["step_s"] / PEAK_BF16_FLOPS,
+                "kernels": pc["kernels"]}
+            log(f"bench: prefill {wc.name}: {pc['step_s'] * 1e3:.4f} ms/step, "
+                f"{other[wc.name]['frac_mfma_peak'] * 100:.1f}% of MFMA peak")
+        log("bench: chunked prefill 0.6B-shape B=2, 512 tokens over 1536 cached")
+        chunk = bench_chunk(args)
+        log(f"bench: chunked prefill {chunk['ms_per_step']:.4f} ms/step, "
+            f"{chunk['frac_mfma_peak'] * 100:.1f}% of MFMA peak")
     dec = None
     if not args.no_decode:
         log("bench: decode 64 sequences, caches 1024..32768")
@@ -483,8 +553,7 @@ def main():
                          "frac": dd["attn_bytes"] / (dd["attn_ms"] / 1e3) / PEAK_HBM_BYTES,
                          "traffic": traffic.get("decode_attention")},
         }
-    dec_window = None
-    if not args.no_decode:
+    if extras and not args.no_decode:
         W = 4096
         log(f"bench: decode, the same 64 sequences in a sliding-window layer (W={W})")
         dw = bench_decode(args, window=W)
@@ -496,8 +565,7 @@ def main():
                       "kernel_ms": dict(zip(q3.STAGES, dw["stage_ms"]))}
         log(f"bench: window decode {dec_window['ms_per_step']:.4f} ms/step, "
             f"{dec_window['frac_hbm_peak'] * 100:.1f}% of HBM peak")
-    dec_paged = None
-    if not args.no_decode:
+    if extras and not args.no_decode:
         log("bench: decode over a paged cache (64-token blocks, shuffled pool)")
         dec_paged = bench_decode_paged(args)
         log(f"bench: paged decode {dec_paged['ms_per_step']:.4f} ms/step, "
@@ -535,6 +603,8 @@ def main():
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": p["flops"][dom] / (dk["avg_ms"] / 1e3) / PEAK_BF16_FLOPS,
                      "traffic": traffic.get("prefill_attention") if dom == "attention" else None},
+        "prefill_per_call": cold,
+        "prefill_other_shapes": other,
         "layer_prefill": layer,
         "chunked_prefill": chunk,
         "decode": dec,

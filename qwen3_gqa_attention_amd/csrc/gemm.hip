@@ -569,9 +569,22 @@ hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const
   if (M <= 64)
     return norm ? launch_gemm<T, 2, 1, 1, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
                 : launch_gemm<T, 2, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
-  if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus)
-    return norm ? launch_gemm<T, 4, 2, 2, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
-                : launch_gemm<T, 4, 2, 2, 4, true>(X, Wqkv, M, N, K, e, se, s);
+  const int t256 = ((M + 255) / 256) * (N / 256), t128 = ((M + 255) / 256) * (N / 128);
+  if (N % 256 == 0 && t256 >= kCus) {
+    // 256x256 tiles unless their last round leaves many CUs idle: one tile
+    // per CU per round, each round costing a fixed ~15 us (prologue,
+    // epilogue, stores) plus the main loop, which is half as long for a
+    // 256x128 tile (measured on the 0.6B, 4B and wide-GQA shapes).
+    const float k = (float)K;
+    const float c256 = (float)((t256 + kCus - 1) / kCus) * (15.f + 0.0245f * k);
+    const float c128 = (float)((t128 + kCus - 1) / kCus) * (15.f + 0.0125f * k);
+    if (c256 <= c128)
+      return norm ? launch_gemm<T, 4, 2, 2, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
+                  : launch_gemm<T, 4, 2, 2, 4, true>(X, Wqkv, M, N, K, e, se, s);
+  }
+  if (t128 >= kCus)  // 256x128 tiles of eight 32x128 waves
+    return norm ? launch_gemm<T, 8, 1, 1, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
+                : launch_gemm<T, 8, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
   return norm ? launch_gemm<T, 4, 1, 1, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
               : launch_gemm<T, 4, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
 }
@@ -591,7 +604,10 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
     return hipGetLastError();
   }
   if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, false>(A, W, M, N, K, qe, se, s);
-  if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus)
+  // 256x256 tiles once they occupy at least half the CUs: with the long K
+  // of o_proj a 256x256 tile beats four 128x128 ones even at 160 tiles
+  // (4B shape: 95 against 101 us).
+  if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus / 2)
     return launch_gemm<T, 4, 2, 2, 4, false>(A, W, M, N, K, qe, se, s);
   if (N % 128 == 0 && ((M + 127) / 128) * (N / 128) >= kCus)
     return launch_gemm<T, 2, 2, 2, 2, false>(A, W, M, N, K, qe, se, s);

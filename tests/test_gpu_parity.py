@@ -393,6 +393,32 @@ def test_layer_prefill_parity(idx, B, T):
     blk.close()
 
 
+def test_layer_prefill_full_size_4b_sampled_rows():
+    # The 4B shape at full size (T=4096): the q/k/v GEMM with the fused input
+    # norm on 256x128 tiles and o_proj with the residual on 256x256 tiles.
+    import torch
+    w = WORKLOADS[3]
+    say(f"layer prefill parity full size, sampled rows: {w.name}")
+    inp = prefill_inputs(w)
+    g_in = input_gain(w, w.d, 23)
+    blk = layer_block(inp, w, g_in)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    kc = torch.empty((1, w.n_kv, w.T, 128), dtype=x.dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    y = host(blk.prefill(x, pos, kc, vc))
+    torch.cuda.synchronize()
+    ts = [0, 1, 255, 256, 2047, 4095]
+    xn = oracle.rms_norm(inp["X"].astype(np.float64), g_in, EPS)
+    ref = oracle.prefill_rows(xn, inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], inp["gq"], inp["gk"],
+                              inp["positions"], [(0, t) for t in ts], n_q=w.n_q, n_kv=w.n_kv,
+                              eps=EPS, theta=ROPE_THETA)
+    assert_close(host(kc)[0], ref["Kc"][0], w.dtype, "k cache (all tokens)")
+    assert_close(np.stack([y[0, t] for t in ts]),
+                 ref["Y"] + inp["X"][0, ts].astype(np.float64), w.dtype, "layer Y at sampled rows")
+    blk.close()
+
+
 @pytest.mark.parametrize("dtype,N", [("bf16", 8), ("f32", 8), ("bf16", 100)])
 def test_layer_decode_parity(dtype, N):
     import torch
