@@ -138,9 +138,9 @@ size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
  * Workspace layout after the call (informative, for tests): the rotated
  * queries [B*T, n_q*d_head], stored multiplied by log2(e)/sqrt(d_head)
  * (the factor the attention kernels need in front of their exp2), then the
- * merged attention output
- * [B*T, n_q*d_head], both of the dtype, each padded to 256 bytes, then the
- * RoPE (cos, sin) table [B*T, d_head/2] in fp32. */
+ * merged attention output [B*T, n_q*d_head], both of the dtype, each padded
+ * to 256 bytes, then (few query tiles only) fp32 partial results of the
+ * attention's key-range split. */
 qwen3_attn_status qwen3_attn_forward_prefill(qwen3_attn_t* h, const void* hidden,
                                              const int32_t* positions,
                                              void* k_cache, void* v_cache,

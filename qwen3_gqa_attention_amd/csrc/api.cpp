@@ -52,7 +52,7 @@ qwen3_attn_status check_desc(const qwen3_attn_desc* d) {
 }
 
 struct WsLayout {
-  size_t q_off, a_off, cs_off, acc_off, ml_off, part_off, total;
+  size_t q_off, a_off, acc_off, ml_off, part_off, total;
   int nchunk;
   bool part;  // decode projections run split-K through the part region
 };
@@ -68,11 +68,10 @@ bool ws_layout_prefill(const qwen3_attn_desc* d, int32_t B, int32_t n_tok, int32
   const size_t qb = align_up((size_t)n_tok * hq * es);
   L->q_off = 0;
   L->a_off = qb;
-  L->cs_off = 2 * qb;
   L->acc_off = L->ml_off = 0;
   L->nchunk = 0;
   L->part = false;
-  L->part_off = L->cs_off + align_up((size_t)n_tok * 64 * 2 * sizeof(float));
+  L->part_off = 2 * qb;
   L->total = L->part_off +
              align_up(q3::flash_partial_floats(B, max_T, d->n_q, d->n_kv, n_tok) * sizeof(float));
   return true;
@@ -96,8 +95,7 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
   const size_t qb = align_up((size_t)n * hq * es);
   L->q_off = 0;
   L->a_off = qb;
-  L->cs_off = 2 * qb;
-  L->acc_off = L->cs_off + align_up((size_t)n * 64 * 2 * sizeof(float));
+  L->acc_off = 2 * qb;
   L->ml_off = L->acc_off + align_up(slots * 128 * sizeof(float));
   L->part_off = L->ml_off + align_up(slots * 2 * sizeof(float));
   L->part = n <= 64;
@@ -152,16 +150,13 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   const int hq = d.n_q * 128;
   T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
-  float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
-  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
+  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
                     d.n_q, d.n_kv, kv, T_len, 0, d.eps, past,
                     h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2, cu_seqlens, B};
   mark(h, s, 0);
-  hipError_t r = q3::launch_rope_table(positions, h->inv_freq, cs, M, s);
-  if (r != hipSuccess) return QWEN3_ATTN_EHIP;
-  r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
+  hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), M, nqkv, d.d_model,
-                                        e, s, nullptr, h->inv_freq);
+                                        e, s, nullptr);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 1);
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
@@ -186,20 +181,14 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   const int hq = d.n_q * 128;
   T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
-  float2* cs = reinterpret_cast<float2*>(ws + L.cs_off);
-  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, cs,
+  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
                     d.n_q, d.n_kv, kv, 1, 1, d.eps, nullptr,
                     h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2};
   mark(h, s, 0);
   float* part = L.part ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
-  hipError_t r = hipSuccess;
-  if (!part) {  // the split-K finishing kernel evaluates RoPE itself
-    r = q3::launch_rope_table(positions, h->inv_freq, cs, N, s);
-    if (r != hipSuccess) return QWEN3_ATTN_EHIP;
-  }
-  r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
+  hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), N, nqkv, d.d_model,
-                                        e, s, part, h->inv_freq);
+                                        e, s, part);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   q3::DecodeScratch sc{reinterpret_cast<float*>(ws + L.acc_off),
                        reinterpret_cast<float*>(ws + L.ml_off), L.nchunk,

@@ -14,15 +14,15 @@
 // of d_head = 128, so the epilogue sees whole heads.  With the 32x32
 // accumulator layout a lane holds columns c, c+32, c+64, c+96 of its rows:
 // the RoPE pair (c, c+64) is lane-local and the head's sum of squares is a
-// 32-lane DPP/swizzle reduction.  cos/sin come from a per-call table
-// (rope_table_kernel): one evaluation per (token, frequency) instead of one
-// per (token, frequency, head).
+// 32-lane DPP/swizzle reduction.  cos/sin are evaluated in the epilogue from
+// the row's position (rope_sincos: exact reduction to a fraction of a
+// revolution, then the hardware sin/cos).
 //
-// Staging: global -> VGPR (16-byte loads) -> LDS, double buffered.  LDS rows
-// are 128 bytes, unpadded, with the 16-byte chunk c of row r stored at chunk
+// Staging: direct global -> LDS loads, double buffered.  LDS rows are 128
+// bytes, unpadded, with the 16-byte chunk c of row r stored at chunk
 // c ^ ((r >> 1) & 7): the 16-byte writes of 8 lanes per row and the
 // 16-byte fragment reads of 16 consecutive rows both hit distinct banks.  The
-// next k-tile's global loads are in flight during the current tile's MFMAs.
+// next k-tile's loads are in flight during the current tile's MFMAs.
 // Results leave through LDS as well, so every global store is 16 bytes of a
 // row.  Workgroups are mapped so that each XCD (workgroups are dealt
 // round-robin over the 8 XCDs) works on a compact block of tiles, which keeps
@@ -63,25 +63,6 @@ __device__ __forceinline__ void rope_sincos(int pos, float whi, float wlo, float
   const float f = __builtin_amdgcn_fractf(__builtin_amdgcn_fractf(r) + e);
   *s = __builtin_amdgcn_sinf(f);
   *c = __builtin_amdgcn_cosf(f);
-}
-
-// cs[row][i] = (cos, sin) of positions[row] * omega_i, i < 64.
-__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restrict__ positions,
-                                                         const float* __restrict__ inv_freq,
-                                                         float2* __restrict__ cs, int M) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= M * 64) return;
-  const int row = idx >> 6, i = idx & 63;
-  float s, c;
-  rope_sincos(positions[row], inv_freq[i], inv_freq[64 + i], &s, &c);
-  cs[idx] = make_float2(c, s);
-}
-
-hipError_t launch_rope_table(const int32_t* positions, const float* inv_freq, float2* cs, int M,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(rope_table_kernel, dim3((M * 64 + 255) / 256), dim3(256), 0, s, positions,
-                     inv_freq, cs, M);
-  return hipGetLastError();
 }
 
 // Linear workgroup id -> (m tile, n tile): XCD x gets the contiguous range
@@ -329,14 +310,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
         gain[ni] = to_f32<T>(g[ni * 32 + c32]) * (kind == 0 ? qe.q_scale : 1.f);
+      // frequencies c32 and 32 + c32 of this lane, as revolutions (hi + lo)
+      const float w0h = qe.rope_rev[c32], w0l = qe.rope_rev[64 + c32];
+      const float w1h = qe.rope_rev[32 + c32], w1l = qe.rope_rev[96 + c32];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         float2 cs0[16], cs1[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
-          cs0[i] = qe.rope_cs[(size_t)row * 64 + c32];
-          cs1[i] = qe.rope_cs[(size_t)row * 64 + 32 + c32];
+          const int pos = qe.positions[row];
+          rope_sincos(pos, w0h, w0l, &cs0[i].y, &cs0[i].x);
+          rope_sincos(pos, w1h, w1l, &cs1[i].y, &cs1[i].x);
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -455,8 +440,7 @@ int small_m_partial_floats(int M, int N, int K, int es) {
 // evaluated here from positions and omega / (2 pi) (hi + lo floats).
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
-                                                         int M, int N, int K, QkvEpilogue qe,
-                                                         const float* __restrict__ inv_freq) {
+                                                         int M, int N, int K, QkvEpilogue qe) {
   const int head = blockIdx.x;
   const int tid = threadIdx.x, j = tid & 15;
   const int row = blockIdx.y * 16 + (tid >> 4);
@@ -509,7 +493,7 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
     for (int e = 0; e < 8; ++e) {
       const int f = (j & 7) * 8 + e;
       float sn, cn;
-      rope_sincos(pos, inv_freq[f], inv_freq[64 + f], &sn, &cn);
+      rope_sincos(pos, qe.rope_rev[f], qe.rope_rev[64 + f], &sn, &cn);
       const float other = dpp_move<0x128>(v[e]);
       v[e] = (j < 8) ? v[e] * cn - other * sn : v[e] * cn + other * sn;
     }
@@ -554,7 +538,7 @@ constexpr int kCus = 256;
 // waits).  Mid-size: 128x128 tiles.  Decode-sized M <= 64: 64x128 tiles.
 template <typename T>
 hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const QkvEpilogue& e,
-                           hipStream_t s, float* part, const float* inv_freq) {
+                           hipStream_t s, float* part) {
   StoreEpilogue se{nullptr, 0, nullptr};
   if (M <= kSmallM && part) {
     const int ks = small_m_ksplit<T>(N, K);
@@ -562,7 +546,7 @@ hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const
     hipError_t r = launch_gemm<T, 2, 1, 1, 4, false, true>(X, Wqkv, M, N, K, e, ps, s, ks);
     if (r != hipSuccess) return r;
     hipLaunchKernelGGL(qkv_finish_kernel<T>, dim3(N / kHeadDim, (M + 15) / 16), dim3(256), 0, s,
-                       part, ks, M, N, K, e, inv_freq);
+                       part, ks, M, N, K, e);
     return hipGetLastError();
   }
   const bool norm = e.in_norm_x != nullptr;
@@ -617,9 +601,9 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
 }
 
 template hipError_t launch_qkv_gemm<float>(const float*, const float*, int, int, int,
-                                           const QkvEpilogue&, hipStream_t, float*, const float*);
+                                           const QkvEpilogue&, hipStream_t, float*);
 template hipError_t launch_qkv_gemm<bf16_t>(const bf16_t*, const bf16_t*, int, int, int,
-                                            const QkvEpilogue&, hipStream_t, float*, const float*);
+                                            const QkvEpilogue&, hipStream_t, float*);
 template hipError_t launch_proj_gemm<float>(const float*, const float*, float*, int, int, int,
                                             hipStream_t, float*, const float*);
 template hipError_t launch_proj_gemm<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, int, int, int,

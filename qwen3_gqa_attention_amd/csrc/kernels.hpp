@@ -41,7 +41,7 @@ struct QkvEpilogue {
   const int32_t* positions;  // [rows] position of each row (decode: its cache slot)
   const void* gq;            // [128] q_norm gain (dtype of the block)
   const void* gk;            // [128] k_norm gain
-  const float2* rope_cs;     // [rows][64] (cos, sin) of position * omega_i
+  const float* rope_rev;     // [128] omega_i / (2 pi) as hi [0..63] + lo [64..127] floats
   int n_q, n_kv;
   KvAddr kv;                 // cache addressing (contiguous or paged)
   int rows_per_seq;          // prefill: T (slot = past + row % T); decode: 1
@@ -85,19 +85,13 @@ struct QkvEpilogue {
   }
 };
 
-// cs[row][i] = (cos, sin)(positions[row] * omega_i), i < 64, with omega_i / (2 pi)
-// given as hi [0..63] + lo [64..127] floats in inv_freq.
-hipError_t launch_rope_table(const int32_t* positions, const float* inv_freq, float2* cs, int M,
-                             hipStream_t s);
-
 // q/k/v projection X[M,K] * Wqkv[N,K]^T with the fused epilogue; N = (n_q + 2 n_kv) * 128.
 // `part` (may be null): fp32 scratch of small_m_partial_floats(M, N, K) floats;
-// with it, M <= 64 runs as a split-K GEMM plus a finishing kernel, which
-// evaluates RoPE from `inv_freq` itself (e.rope_cs is not read then).
+// with it, M <= 64 runs as a split-K GEMM plus a finishing kernel that
+// applies the epilogue.
 template <typename T>
 hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K,
-                           const QkvEpilogue& e, hipStream_t s, float* part,
-                           const float* inv_freq);
+                           const QkvEpilogue& e, hipStream_t s, float* part);
 
 // Plain projection C[M,N] = A[M,K] * W[N,K]^T (o_proj); `part` as above;
 // `residual` (may be null, layout of C) is added in fp32 before rounding.

@@ -80,14 +80,14 @@ def align(x):
 
 def test_workspace_size_prefill_and_decode(built_lib):
     d = desc()
-    # prefill: rotated q, merged attention output, RoPE (cos, sin) table
-    assert q3.qwen3_attn_workspace_size(d, 0, 2, 2048, 0) == 2 * align(2 * 2048 * 2048 * 2) + align(4096 * 64 * 8)
+    # prefill: rotated q and merged attention output (512 query tiles: no key split)
+    assert q3.qwen3_attn_workspace_size(d, 0, 2, 2048, 0) == 2 * align(2 * 2048 * 2048 * 2)
     d32 = desc(dtype=q3.QWEN3_ATTN_F32)
     # B=1, T=128: 16 query-tile workgroups (< 256), so each key range is split
     # 8 ways and the fp32 partials (O, then m and l) are reserved as well
     part = 8 * 128 * 16 * (128 + 2) * 4
     assert (q3.qwen3_attn_workspace_size(d32, 0, 1, 128, 0)
-            == 2 * align(128 * 2048 * 4) + align(128 * 64 * 8) + align(part))
+            == 2 * align(128 * 2048 * 4) + align(part))
     # decode: q and merged output, then per-chunk partials (512-key chunks)
     cap, N = 32832, 64
     nchunk = -(-cap // 512)
@@ -95,8 +95,7 @@ def test_workspace_size_prefill_and_decode(built_lib):
     # split-K partials of the 64-row projections: q/k/v 8 slices x 64 x 4096,
     # o_proj 32 slices x 64 x 1024 (fp32); the larger is reserved
     part = max(8 * 64 * 4096, 32 * 64 * 1024) * 4
-    want = (2 * align(N * 2048 * 2) + align(N * 64 * 8) + align(slots * 128 * 4) + align(slots * 2 * 4)
-            + align(part))
+    want = 2 * align(N * 2048 * 2) + align(slots * 128 * 4) + align(slots * 2 * 4) + align(part)
     assert q3.qwen3_attn_workspace_size(d, 1, N, 1, cap) == want
 
 
