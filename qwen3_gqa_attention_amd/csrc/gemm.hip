@@ -90,10 +90,13 @@ __device__ __forceinline__ int swz(int row, int k) {
   return row * (8 * EPC) + ((((k / EPC) ^ (row >> 1)) & 7) * EPC) + (k % EPC);
 }
 
-// NORM (q/k/v only): the input rows are RMS-normalised on the fly -- the
-// gain is folded into the weights, and the sum of squares of each A row is
-// accumulated from the A fragments the MFMAs consume, so 1/rms(row) scales
-// the accumulators in the epilogue.
+// NORM selects the decoder-layer variant.  q/k/v: the input rows are
+// RMS-normalised on the fly -- the gain is folded into the weights, and the
+// sum of squares of each A row is accumulated from the A fragments the MFMAs
+// consume, so 1/rms(row) scales the accumulators in the epilogue.  Plain
+// projection: the residual (se.residual) is added to the fp32 accumulators
+// before the single rounding.  A compile-time switch, so the plain kernels
+// carry none of this (the residual loads would raise register pressure).
 template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false,
           int NSTAGE = 2, bool NORM = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restrict__ A,
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = MF::run(af[ks & 1][mi], bfr[ks & 1][ni], acc[mi][ni]);
-      if constexpr (NORM) {
+          if constexpr (NORM && QKV) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) ssq[mi] = frag_sumsq(af[ks & 1][mi], ssq[mi]);
       }
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
       }
     return;
   }
-  if constexpr (NORM) {
+  if constexpr (NORM && QKV) {
     // Lane l holds half of row (l % 32)'s sum of squares; the accumulator
     // element i of lane l belongs to row mfma32_row(i, l).
 #pragma unroll
@@ -284,18 +287,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
       }
     }
   }
-  if constexpr (!QKV) {
-    if (se.residual) {
-      const T* res = reinterpret_cast<const T*>(se.residual);
+  if constexpr (!QKV && NORM) {
+    const T* res = reinterpret_cast<const T*>(se.residual);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
+      for (int i = 0; i < 16; ++i) {
+        const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni][i] += to_f32<T>(res[(size_t)row * se.ldc + n0 + wn * 32 * NI + ni * 32 + c32]);
-        }
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni][i] += to_f32<T>(res[(size_t)row * se.ldc + n0 + wn * 32 * NI + ni * 32 + c32]);
+      }
+      // one 32-row block's residual loads at a time: bounds the registers
+      // they hold in flight
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   int head = 0, kind = 3;  // kind 3: plain projection output
@@ -578,6 +583,7 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
                             float* part, const T* residual) {
   QkvEpilogue qe{};
   StoreEpilogue se{C, N, residual};
+  const bool res = residual != nullptr;
   if (M <= kSmallM && part) {
     const int ks = small_m_ksplit<T>(N, K);
     StoreEpilogue ps{part, N, nullptr};
@@ -587,17 +593,22 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
                        ks, M * N, C, residual);
     return hipGetLastError();
   }
-  if (M <= 64) return launch_gemm<T, 2, 1, 1, 4, false>(A, W, M, N, K, qe, se, s);
+  if (M <= 64)
+    return res ? launch_gemm<T, 2, 1, 1, 4, false, false, 2, true>(A, W, M, N, K, qe, se, s)
+               : launch_gemm<T, 2, 1, 1, 4, false>(A, W, M, N, K, qe, se, s);
   // 256x256 tiles once they occupy at least half the CUs: with the long K
   // of o_proj a 256x256 tile beats four 128x128 ones even at 160 tiles
   // (4B shape: 95 against 101 us).
   if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus / 2)
-    return launch_gemm<T, 4, 2, 2, 4, false>(A, W, M, N, K, qe, se, s);
+    return res ? launch_gemm<T, 4, 2, 2, 4, false, false, 2, true>(A, W, M, N, K, qe, se, s)
+               : launch_gemm<T, 4, 2, 2, 4, false>(A, W, M, N, K, qe, se, s);
   if (N % 128 == 0 && ((M + 127) / 128) * (N / 128) >= kCus)
-    return launch_gemm<T, 2, 2, 2, 2, false>(A, W, M, N, K, qe, se, s);
+    return res ? launch_gemm<T, 2, 2, 2, 2, false, false, 2, true>(A, W, M, N, K, qe, se, s)
+               : launch_gemm<T, 2, 2, 2, 2, false>(A, W, M, N, K, qe, se, s);
   // Too few 128x128 tiles to fill the chip (e.g. o_proj of a 1024-token
   // chunk): 64x64 tiles, four 32x32 waves (N is a multiple of 64).
-  return launch_gemm<T, 2, 2, 1, 1, false>(A, W, M, N, K, qe, se, s);
+  return res ? launch_gemm<T, 2, 2, 1, 1, false, false, 2, true>(A, W, M, N, K, qe, se, s)
+             : launch_gemm<T, 2, 2, 1, 1, false>(A, W, M, N, K, qe, se, s);
 }
 
 template hipError_t launch_qkv_gemm<float>(const float*, const float*, int, int, int,
