@@ -455,15 +455,22 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = 0.f;
-  for (int k = 0; k < ks; ++k) {
-    const float* p = part + ((size_t)k * M + r) * N + head * kHeadDim + j * 8;
-    const f32x4_v x0 = *reinterpret_cast<const f32x4_v*>(p);
-    const f32x4_v x1 = *reinterpret_cast<const f32x4_v*>(p + 4);
+  for (int k0 = 0; k0 < ks; k0 += 4) {  // four slices' loads in flight at once
+    f32x4_v x[4][2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] += x0[e];
-      v[4 + e] += x1[e];
+    for (int u = 0; u < 4; ++u) {
+      const float* p = part + ((size_t)(k0 + u) * M + r) * N + head * kHeadDim + j * 8;
+      const bool in = k0 + u < ks;
+      x[u][0] = in ? *reinterpret_cast<const f32x4_v*>(p) : f32x4_v{0.f, 0.f, 0.f, 0.f};
+      x[u][1] = in ? *reinterpret_cast<const f32x4_v*>(p + 4) : f32x4_v{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] += x[u][0][e];
+        v[4 + e] += x[u][1][e];
+      }
   }
   if (qe.in_norm_x) {
     // Input RMSNorm (gain folded into the weights): 1/rms of the row of x,
@@ -526,8 +533,18 @@ __global__ __launch_bounds__(64) void sum_partials_kernel(const float* __restric
                                                           const T* __restrict__ residual) {
   const int i = (blockIdx.x * 64 + threadIdx.x) * 4;
   if (i >= MN) return;
-  f32x4_v a = *reinterpret_cast<const f32x4_v*>(part + i);
-  for (int k = 1; k < ks; ++k) a += *reinterpret_cast<const f32x4_v*>(part + (size_t)k * MN + i);
+  // Eight slices' loads in flight at once (a plain loop leaves the latency
+  // of each exposed); the sum keeps slice order.
+  f32x4_v a = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < ks; k0 += 8) {
+    f32x4_v v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = k0 + u < ks ? *reinterpret_cast<const f32x4_v*>(part + (size_t)(k0 + u) * MN + i)
+                         : f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += v[u];
+  }
   if (residual) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] += to_f32<T>(residual[i + j]);
