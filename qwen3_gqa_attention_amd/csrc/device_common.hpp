@@ -117,6 +117,21 @@ __device__ __forceinline__ void dma16_to_lds(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                : : "v"(g), "s"(lds_base) : "memory", "m0");
 }
+// The same load addressed as a wave-uniform base (kept in SGPRs) plus a
+// per-lane 32-bit byte offset: no 64-bit address arithmetic per lane.
+// `sbase` must be the same in every lane; it is read from the first active
+// lane so that the compiler keeps it in scalar registers.
+__device__ __forceinline__ void dma16_to_lds_sv(const void* sbase, uint32_t voff,
+                                                uint32_t lds_base) {
+  // (readfirstlane returns a signed int: each half goes through uint32_t so
+  // that widening zero-extends it)
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint64_t u = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               : : "v"(voff), "s"(u), "s"(lds_base) : "memory", "m0");
+}
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(

@@ -31,6 +31,8 @@
 //                               keys are one 16-byte LDS read.
 // fp32 storage uses the 32x32x2 f32 MFMA with the same structure; there V is
 // staged untransposed, since each lane reads a single element.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // Chunked prefill: the sequence already holds P cached tokens, chunk token
   // t is key P + t and sees keys 0 .. P + t (P = 0 for a first prefill).
   const int P = past ? past[b] : 0;
-  const int S_len = P + Tb;
+  const int S_len = __builtin_amdgcn_readfirstlane(P + Tb);
 
   // Wave w owns query block w & 3 (32 rows) over key half w >> 2 (with
   // KSPLIT = 2; with KSPLIT = 1 four waves cover the whole key range).
@@ -171,29 +173,42 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // finite); the causal mask zeroes their weight.
   const int hw = wave & 3;  // wave index inside its key half
   constexpr int NDMA = VT ? BN / 16 : 1;  // DMA instructions per wave per tile (K and V each)
-  int dma_row[NDMA], dk_ch[NDMA], dv_ch[NDMA];  // lane's tile row and swizzled chunk offsets
+  constexpr uint32_t ROWB = kHeadDim * sizeof(T);  // bytes per cache row
+  // Byte offset, from the tile's first row, of the 16 bytes this lane fetches
+  // in DMA instruction j of a full tile (row dma_row(j), swizzled chunk).
+  auto dma_row = [&](int j) { return (j * 4 + hw) * 4 + (lane >> 4); };
+  uint32_t dk_off[NDMA], dv_off[NDMA];
 #pragma unroll
   for (int j = 0; j < NDMA; ++j) {
-    const int r = (j * 4 + hw) * 4 + (lane >> 4);
-    dma_row[j] = r;
-    dk_ch[j] = ((lane & 15) ^ (r & 15)) * EPC;
-    dv_ch[j] = ((lane & 15) ^ (4 * (r & 3))) * EPC;
+    const int r = dma_row(j);
+    dk_off[j] = r * ROWB + ((lane & 15) ^ (r & 15)) * 16;
+    dv_off[j] = r * ROWB + ((lane & 15) ^ (4 * (r & 3))) * 16;
   }
   const uint32_t smem_lds = lds_addr(smem);
   auto dma_tile = [&](int kt, int buf) {
-    const int kbase = kt * BN;
+    // Everything but the lane offsets is wave-uniform and kept scalar.
+    const int kbase = __builtin_amdgcn_readfirstlane(kt * BN);
     const uint32_t lk = smem_lds + (uint32_t)((Ks(buf) - smem) * sizeof(T));
     const uint32_t lv = smem_lds + (uint32_t)((Vs(buf) - smem) * sizeof(T));
-    const bool full = kbase + BN <= S_len;  // uniform
+    // the tile's first row: one uniform base per tile, per-lane 32-bit offsets
     const int64_t r0 = tile_row(kbase);
+    const T* kt_base = Kc + r0 * kHeadDim;
+    const T* vt_base = Vc + r0 * kHeadDim;
+    if (kbase + BN <= S_len) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) {
-      const int r = full ? dma_row[j] : min(kbase + dma_row[j], S_len - 1) - kbase;
-      const T* krow = Kc + (r0 + r) * kHeadDim;
-      const T* vrow = Vc + (r0 + r) * kHeadDim;
-      const uint32_t r4b = (uint32_t)((j * 4 + hw) * 4 * LDK * sizeof(T));  // this instruction's first row
-      dma16_to_lds(krow + dk_ch[j], lk + r4b);
-      dma16_to_lds(vrow + dv_ch[j], lv + r4b);
+      for (int j = 0; j < NDMA; ++j) {
+        const uint32_t r4b = (uint32_t)((j * 4 + hw) * 4 * LDK * sizeof(T));  // instruction's first row
+        dma16_to_lds_sv(kt_base, dk_off[j], lk + r4b);
+        dma16_to_lds_sv(vt_base, dv_off[j], lv + r4b);
+      }
+    } else {  // last tile: rows past the sequence re-read its last row
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const uint32_t back = dma_row(j) - (min(kbase + dma_row(j), S_len - 1) - kbase);
+        const uint32_t r4b = (uint32_t)((j * 4 + hw) * 4 * LDK * sizeof(T));
+        dma16_to_lds_sv(kt_base, dk_off[j] - back * ROWB, lk + r4b);
+        dma16_to_lds_sv(vt_base, dv_off[j] - back * ROWB, lv + r4b);
+      }
     }
   };
 
@@ -230,7 +245,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_v mbias = f32x16_v{};
 
-  // One key tile from LDS stage `buf`.
+  // One key tile from stage P (0 or 1, a compile-time constant) of this
+  // wave's key half.
   // Per-lane LDS element offsets of the fragment reads, fixed for the whole
   // key loop (the swizzles depend on the lane only): k_off[ks] for the K
   // fragment of MFMA step ks, v_off[db] for the first transposing V read of
@@ -251,7 +267,19 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     }
   }
 
-  auto tile = [&](int kt, int buf) {
+  // Fragment addresses in stage 0 of this wave's key half, loop-invariant;
+  // stage 1 and the other key blocks / rows are compile-time offsets, which
+  // the LDS reads take as immediates (no address arithmetic per tile).
+  const T* kfrag[NKOFF];
+  const T* vfrag[4];
+#pragma unroll
+  for (int ks = 0; ks < NKOFF; ++ks) kfrag[ks] = Ks(kh * 2) + k_off[ks];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vfrag[db] = Vs(kh * 2) + v_off[db];
+
+  auto tile = [&](int kt, auto stage) {
+    constexpr int P = decltype(stage)::value;
+    const int buf = kh * 2 + P;
     if (wave_active && kt * BN <= w_tok_hi && kt * BN + BN - 1 >= w_key_lo) {
       // S^T = K Q^T - m_run.  Q carries the log2(e)/sqrt(d) factor, so the
       // scores are already in the base-2 units of the exponent.
@@ -261,9 +289,9 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
       const T* ks_ptr = Ks(buf);
       // The first MFMA step of each chain adds to mbias instead of zero.
       // element offset of this lane's K fragment for MFMA step ks
-      auto koff = [&](int ks) {
-        if constexpr (VT) return k_off[ks];
-        else return c32 * LDK + ks * MF::K + hk * MF::KL;
+      auto kfr = [&](int ks, int kb) -> const T* {
+        if constexpr (VT) return kfrag[ks] + P * KSZ + kb * 32 * LDK;
+        else return ks_ptr + c32 * LDK + ks * MF::K + hk * MF::KL + kb * 32 * LDK;
       };
       // K fragments are read KPF steps ahead of their MFMAs (a ring of KPF+1
       // register sets): one step's NKB MFMAs are shorter than an LDS read.
@@ -272,7 +300,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
 #pragma unroll
       for (int p = 0; p < KPF; ++p)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kf[p][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(p));
+        for (int kb = 0; kb < NKB; ++kb) kf[p][kb] = MF::load(kfr(p, kb));
       // The scheduler would sink the reads next to their MFMAs; pin the
       // order: the prologue reads first, then each MFMA followed by one read
       // KPF steps ahead.
@@ -282,7 +310,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
         if (ks + KPF < DSTEPS) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            kf[(ks + KPF) % (KPF + 1)][kb] = MF::load(ks_ptr + kb * 32 * LDK + koff(ks + KPF));
+            kf[(ks + KPF) % (KPF + 1)][kb] = MF::load(kfr(ks + KPF, kb));
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -297,16 +325,27 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
           __builtin_amdgcn_sched_group_barrier(0x008, NKB, 0);
         }
       }
-      // causal mask (only tiles that cross this wave's diagonal) and the
-      // window's lower edge (only tiles that cross it), then the running max
-      if (kt * BN + BN - 1 > w_tok_lo || kt * BN < w_mask_lo) {
+      // Causal mask (only tiles that cross this wave's diagonal) and the
+      // window's lower edge (only tiles that cross it).  Element (kb, i) of
+      // this lane is key kt*BN + 4*hk + c with the constant
+      // c = kb*32 + 8*(i/4) + i%4, so each test is one compare of a
+      // constant against a per-lane limit.
+      const int key0 = kt * BN + 4 * hk;
+      if (kt * BN + BN - 1 > w_tok_lo) {
+        const int lim = tok - key0;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt * BN + kb * 32 + mfma32_row(i, lane);
-            if (key > tok || key < key_lo) s[kb][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
+      }
+      if (kt * BN < w_mask_lo) {
+        const int lo = key_lo - key0;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + 8 * (i >> 2) + (i & 3) < lo) s[kb][i] = -INFINITY;
       }
       // Tile max relative to the running max; the two half-waves hold the
       // two halves of each query's keys.
@@ -368,7 +407,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
             // transposing reads of the row-major V tile.  In each read,
             // lane j of a 16-lane group addresses key K0 + j/4, dims
             // D0 + 4*(j%4) .. +3, and receives dim D0 + j of keys K0 .. K0+3.
-            const T* vq = Vs(buf) + v_off[db] + ks2 * 16 * LDV;
+            const T* vq = vfrag[db] + P * VSZ + ks2 * 16 * LDV;
             const v4bf16_t lo = ds_read_tr16(vq);
             const v4bf16_t hi = ds_read_tr16(vq + 8 * LDV);
             const bf16x8_v vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -401,23 +440,31 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // i+2's global loads are issued while tile i runs, and tile i+1 (loaded one
   // iteration earlier) is staged after it.  Both halves run n0 iterations so
   // every wave meets every barrier.
-  const int n0 = KSPLIT == 2 ? (ntiles + 1) / 2 : ntiles;
-  const int base = t_lo + (kh ? n0 : 0);
-  const int cnt = kh ? ntiles - n0 : n0;
+  // (uniform; read from the first lane so the loop control stays scalar)
+  const int n0 = __builtin_amdgcn_readfirstlane(KSPLIT == 2 ? (ntiles + 1) / 2 : ntiles);
+  const int base = __builtin_amdgcn_readfirstlane(t_lo + (kh ? n0 : 0));
+  const int cnt = __builtin_amdgcn_readfirstlane(kh ? ntiles - n0 : n0);
   const int s0 = kh * 2, s1 = kh * 2 + 1;
   if constexpr (VT) {
     // Two LDS stages per key half: tile i+1's loads are issued before tile i
     // runs into the stage that tile i-1 used (free once every wave passed the
     // barrier that ended tile i-1).  Both halves run n0 iterations so every
     // wave meets every barrier.
+    // Unrolled by two so that each copy reads a fixed stage: tile i sits in
+    // stage i % 2 of the half.
+    auto step = [&](int i, auto stage) {
+      constexpr int P = decltype(stage)::value;
+      if (i + 1 < cnt) dma_tile(base + i + 1, P ? s0 : s1);
+      if (i < cnt) tile(base + i, stage);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i+1 has landed
+      lds_barrier();
+    };
     if (cnt > 0) dma_tile(base, s0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and tile 0
     lds_barrier();
-    for (int i = 0; i < n0; ++i) {
-      if (i + 1 < cnt) dma_tile(base + i + 1, (i & 1) ? s0 : s1);
-      if (i < cnt) tile(base + i, (i & 1) ? s1 : s0);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i+1 has landed
-      lds_barrier();
+    for (int i = 0; i < n0; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      if (i + 1 < n0) step(i + 1, std::integral_constant<int, 1>{});
     }
   } else {
     for (int i = 0; i < n0; ++i) {
@@ -426,7 +473,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
         sstore(s0);
       }
       lds_barrier();
-      if (i < cnt) tile(base + i, s0);
+      if (i < cnt) tile(base + i, std::integral_constant<int, 0>{});
       lds_barrier();
     }
   }
