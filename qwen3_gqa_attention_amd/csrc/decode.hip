@@ -209,49 +209,81 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
   }
 }
 
-// Merge the key chunks of each (sequence, query head): grid (n_q, N), 128
-// threads (one per dim).  One online pass; 16 chunks' partials are loaded
-// together so their latencies overlap.
+// Merge the key chunks of each (sequence, query head): grid (n_q, N), 256
+// threads.  Wave w takes chunks w, w+4, ... in one online pass (8 chunks'
+// partials loaded together so their latencies overlap; each lane holds two
+// of the 128 dims), then the four waves' results are merged through LDS.
 template <typename T>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part_acc,
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_acc,
                                                              const float* __restrict__ part_ml,
                                                              const int32_t* __restrict__ positions,
                                                              T* __restrict__ Out, int n_q, int n_kv,
                                                              int nchunk, int window) {
-  constexpr int U = 16;
-  const int head = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  constexpr int U = 8, NW = 4;
+  const int head = blockIdx.x, s = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n_rep = n_q / n_kv;
   const int g = head / n_rep, r = head % n_rep;
   const int nkeys = positions[s] + 1;
   const int nc = (nkeys + kDecodeChunk - 1) / kDecodeChunk;
   const int c_lo = window > 0 ? max(0, nkeys - window) / kDecodeChunk : 0;  // first chunk written
   const size_t base = (size_t)(s * n_kv + g) * nchunk;
-  float M = -INFINITY, a = 0.f, lt = 0.f;
-  for (int c0 = c_lo; c0 < nc; c0 += U) {
-    float mv[U], lv[U], av[U];
+  float M = -INFINITY, lt = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int c0 = c_lo + wave; c0 < nc; c0 += NW * U) {
+    float mv[U], lv[U];
+    f32x2_v av[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t sl = (base + c0 + u) * n_rep + r;
-      const bool ok = c0 + u < nc;
+      const int c = c0 + NW * u;
+      const size_t sl = (base + c) * n_rep + r;
+      const bool ok = c < nc;
       mv[u] = ok ? part_ml[sl * 2] : -INFINITY;
       lv[u] = ok ? part_ml[sl * 2 + 1] : 0.f;
-      av[u] = ok ? part_acc[sl * kHeadDim + d] : 0.f;
+      av[u] = ok ? *reinterpret_cast<const f32x2_v*>(part_acc + sl * kHeadDim + 2 * lane)
+                 : f32x2_v{0.f, 0.f};
     }
     float mx = M;
 #pragma unroll
-    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);
-    const float sc = exp2f(M - mx);   // 0 on the first pass (M = -inf, mx finite)
-    a *= sc;
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);  // finite: chunk c0 < nc is written
+    const float sc = exp2f(M - mx);   // 0 on the first pass (M = -inf)
+    a0 *= sc;
+    a1 *= sc;
     lt *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float w = exp2f(mv[u] - mx);
-      a = fmaf(w, av[u], a);
+      a0 = fmaf(w, av[u][0], a0);
+      a1 = fmaf(w, av[u][1], a1);
       lt = fmaf(w, lv[u], lt);
     }
     M = mx;
   }
-  Out[(size_t)s * n_q * kHeadDim + head * kHeadDim + d] = from_f32<T>(a / lt);
+  // Waves without a chunk keep M = -inf and contribute nothing; wave 0
+  // always has chunk c_lo.
+  __shared__ float sm_ml[NW][2];
+  __shared__ float sm_a[NW][kHeadDim];
+  if (lane == 0) {
+    sm_ml[wave][0] = M;
+    sm_ml[wave][1] = lt;
+  }
+  sm_a[wave][2 * lane] = a0;
+  sm_a[wave][2 * lane + 1] = a1;
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    const int d = threadIdx.x;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, sm_ml[w][0]);
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_ml[w][0];
+      const float sc = mw == -INFINITY ? 0.f : exp2f(mw - Mx);
+      a = fmaf(sc, sm_a[w][d], a);
+      l = fmaf(sc, sm_ml[w][1], l);
+    }
+    Out[(size_t)s * n_q * kHeadDim + head * kHeadDim + d] = from_f32<T>(a / l);
+  }
 }
 
 template <typename T, int NREP>
@@ -283,7 +315,7 @@ hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(n_q, N), dim3(kHeadDim), 0, s, ws.part_acc,
+  hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(n_q, N), dim3(256), 0, s, ws.part_acc,
                      ws.part_ml, positions, Out, n_q, n_kv, ws.nchunk, window);
   return hipGetLastError();
 }
