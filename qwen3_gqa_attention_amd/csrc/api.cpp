@@ -19,9 +19,9 @@ struct qwen3_attn {
   void* w_o;         // [d, n_q * 128]
   void* g_q;         // [128]
   void* g_k;         // [128]
-  float* inv_freq;   // [128]: omega_i / (2 pi) as hi [0..63] + lo [64..127] floats,
+  float* rope_rev;   // [128]: omega_i / (2 pi) as hi [0..63] + lo [64..127] floats,
                      // omega_i = theta^(-2i/128)
-  float inv_freq_host[128];
+  float rope_rev_host[128];
   int in_norm;       // 1: forward = hidden + block(RMSNorm(hidden) * input gain)
   // measurement aid: events before each kernel and after the last
   int timing_cap;
@@ -150,7 +150,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   const int hq = d.n_q * 128;
   T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
-  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
+  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->rope_rev,
                     d.n_q, d.n_kv, kv, T_len, 0, d.eps, past,
                     h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2, cu_seqlens, B};
   mark(h, s, 0);
@@ -181,7 +181,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
   const int hq = d.n_q * 128;
   T* qbuf = reinterpret_cast<T*>(ws + L.q_off);
   T* abuf = reinterpret_cast<T*>(ws + L.a_off);
-  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->inv_freq,
+  q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->rope_rev,
                     d.n_q, d.n_kv, kv, 1, 1, d.eps, nullptr,
                     h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2};
   mark(h, s, 0);
@@ -244,12 +244,12 @@ qwen3_attn_status create_impl(const qwen3_attn_desc* desc, const qwen3_attn_weig
   h->w_o = p + b_wqkv;
   h->g_q = p + b_wqkv + b_wo;
   h->g_k = p + b_wqkv + b_wo + b_g;
-  h->inv_freq = reinterpret_cast<float*>(p + b_wqkv + b_wo + 2 * b_g);
+  h->rope_rev = reinterpret_cast<float*>(p + b_wqkv + b_wo + 2 * b_g);
   for (int i = 0; i < 64; ++i) {
     const double rev = std::pow(desc->rope_theta, -2.0 * i / 128.0) / (2.0 * M_PI);
     const float hi = static_cast<float>(rev);
-    h->inv_freq_host[i] = hi;
-    h->inv_freq_host[64 + i] = static_cast<float>(rev - static_cast<double>(hi));
+    h->rope_rev_host[i] = hi;
+    h->rope_rev_host[64 + i] = static_cast<float>(rev - static_cast<double>(hi));
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -263,7 +263,7 @@ qwen3_attn_status create_impl(const qwen3_attn_desc* desc, const qwen3_attn_weig
   if (r == hipSuccess) r = hipMemcpyAsync(h->g_q, w->q_norm, 128 * es, hipMemcpyDeviceToDevice, s);
   if (r == hipSuccess) r = hipMemcpyAsync(h->g_k, w->k_norm, 128 * es, hipMemcpyDeviceToDevice, s);
   if (r == hipSuccess)
-    r = hipMemcpyAsync(h->inv_freq, h->inv_freq_host, 128 * sizeof(float), hipMemcpyHostToDevice, s);
+    r = hipMemcpyAsync(h->rope_rev, h->rope_rev_host, 128 * sizeof(float), hipMemcpyHostToDevice, s);
   // Input RMSNorm: (x / rms(x) * g) W^T = (x W'^T) / rms(x) with W' = W * g by
   // columns, so the gain is folded into the q/k/v weights once here.
   h->in_norm = input_norm != nullptr;
@@ -275,7 +275,7 @@ qwen3_attn_status create_impl(const qwen3_attn_desc* desc, const qwen3_attn_weig
             : q3::launch_scale_columns<q3::bf16_t>(static_cast<q3::bf16_t*>(h->w_qkv), rows, cols,
                                                    static_cast<const q3::bf16_t*>(input_norm), s);
   }
-  if (r == hipSuccess) r = hipStreamSynchronize(s);  // host staging of inv_freq must complete
+  if (r == hipSuccess) r = hipStreamSynchronize(s);  // the host copy of rope_rev must complete
   if (r != hipSuccess) {
     (void)hipFree(h->mem);
     delete h;
