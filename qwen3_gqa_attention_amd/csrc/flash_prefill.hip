@@ -239,9 +239,10 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   f32x16_v o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_v{};
-  // m_run: running max of the (log2-scaled) scores, -inf until this lane has
+  // m_run: the reference max of the (log2-scaled) scores, at most kMaxSlack
+  // below their running max (see the rescale below), -inf until this lane has
   // seen a key.  The score accumulators start at -m_run (0 while m_run is
-  // -inf), so they come out of the MFMAs already relative to the running max.
+  // -inf), so they come out of the MFMAs already relative to it.
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_v mbias = f32x16_v{};
 
@@ -359,12 +360,20 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                          __float_as_uint(mloc), false, false);
         mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-      // A lane's max moves if this tile exceeds it, or if it is the lane's
-      // first tile with an unmasked key.  Only then are O and the sum
-      // rescaled and the scores shifted (rare after the first tiles).
+      // m_run is a reference point, not necessarily the exact running max:
+      // O and l are both sums of exp2(s - m_run), so any finite reference
+      // gives the same O / l.  It must be set on a lane's first tile with an
+      // unmasked key, and is raised only once a tile's max exceeds it by more
+      // than kMaxSlack, which keeps every probability below 2^kMaxSlack
+      // (far from fp32 and bf16 overflow).  With 32 queries per wave, the
+      // wave-wide rescale would otherwise run on nearly every tile, because
+      // some query's max moves; with the slack it runs only on the first
+      // tiles.  When it runs, every lane whose max moved catches up.
+      constexpr float kMaxSlack = 8.f;
       const bool first = m_run == -INFINITY;
       const bool moved = first ? (mloc > -INFINITY) : (mloc > 0.f);
-      if (__ballot(moved) != 0) {
+      const bool must = first ? moved : (mloc > kMaxSlack);
+      if (__ballot(must) != 0) {
         const float delta = moved ? mloc : 0.f;
         if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-delta);

@@ -14,8 +14,8 @@ import pytest
 
 import oracle
 from gpu_util import assert_close, block_from_inputs, dev, from_paged, host, say, to_paged
-from workloads import (EPS, ROPE_THETA, WORKLOADS, decode_cache_host, decode_inputs,
-                       prefill_inputs)
+from workloads import (EPS, ROPE_THETA, WORKLOADS, bf16_bits_to_f32, decode_cache_host,
+                       decode_inputs, prefill_inputs, round_to_bf16_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -256,6 +256,46 @@ def test_prefill_chunk_full_size_0p6b():
     ref = oracle_chunk(w, inp, past, kc, vc)
     assert_close(got["Y"], ref["Y"], w.dtype, "block output Y")
     assert_close(got["Kc"][:, :, 1536:], ref["Kc"], w.dtype, "k cache chunk")
+
+
+# fp32: a_j rises for the whole cache and the spike is 3000.  bf16: a_j
+# stops after 4 steps and the spike sits 100 above it -- a score difference
+# between two competing keys carries the bf16 rounding of q~ times their
+# difference in a (relative 2^-9), which must stay well inside the bf16 bar.
+RISE_CASES = [(1, None, 3000.0), (2, 4, 260.0)]
+
+
+@pytest.mark.parametrize("idx,steps,spike", RISE_CASES)
+def test_prefill_chunk_scores_rising_past_the_rescale_slack(idx, steps, spike):
+    # The flash kernel keeps a reference max that may trail a query's running
+    # max by up to 8 (log2 units) and rescales O and the sum only past that.
+    # Cached keys k_j = a_j u_g + e_j, with a_j rising by 40 every 64 keys
+    # (for `steps` steps) and one key at spike * u_g three slots before the
+    # end of sequence 0, make a query's max jump by 40 (q.u) log2(e)/sqrt(d)
+    # per 64 keys: past the slack for some queries, within it for others,
+    # and again at the spike.  Queries with q.u < 0 keep their max in the
+    # first tile, and the chunk's own keys dominate them.
+    w, inp, past, kc, vc = chunk_case(idx, 2, 100, [1000, 700])
+    rng = np.random.default_rng(7)
+    store = (lambda a: bf16_bits_to_f32(round_to_bf16_bits(a.astype(np.float32)))) \
+        if w.dtype == "bf16" else (lambda a: a.astype(np.float32))
+    U = rng.standard_normal((2, w.n_kv, 128))
+    U /= np.linalg.norm(U, axis=-1, keepdims=True)
+    for b, P in enumerate(past):
+        step = np.arange(P) // 64
+        a = 40.0 * (step if steps is None else np.minimum(step, steps))
+        kc[b, :, :P] = store(a[None, :, None] * U[b][:, None, :] + kc[b, :, :P])
+    kc[0, :, past[0] - 3] = store(spike * U[0])
+    say(f"chunked prefill, rising scores: workload {idx} ({w.name}) B=2 T=100 "
+        f"past={past.tolist()} steps={steps} spike={spike}")
+    got = run_chunk_gpu(w, inp, past, kc, vc)
+    ref = oracle_chunk(w, inp, past, kc, vc)
+    # both sides of the slack occur: per-64-key jumps above 8 and in (0, 8]
+    rep = w.n_q // w.n_kv
+    qu = np.einsum("bthd,bhd->bth", ref["Q"], np.repeat(U, rep, axis=1))
+    jump = 40.0 * qu * Q_WS_SCALE
+    assert np.mean(jump > 8) > 0.02 and np.mean((jump > 0) & (jump <= 8)) > 0.2
+    assert_close(got["Y"], ref["Y"], w.dtype, "block output Y")
 
 
 def test_prefill_chunk_argument_errors():
