@@ -97,9 +97,15 @@ __device__ __forceinline__ int swz(int row, int k) {
 // projection: the residual (se.residual) is added to the fp32 accumulators
 // before the single rounding.  A compile-time switch, so the plain kernels
 // carry none of this (the residual loads would raise register pressure).
+//
+// KG = 2 splits the K range of each tile over two groups of WM x WN waves,
+// each with its own LDS stages; group 1 hands its accumulators to group 0
+// through LDS after the main loop, and group 0 runs the epilogue.  Used when
+// there is one tile per CU: two waves per SIMD instead of one, so one wave's
+// MFMAs cover the other's LDS and barrier waits.
 template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false,
-          int NSTAGE = 2, bool NORM = false>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restrict__ A,
+          int NSTAGE = 2, bool NORM = false, int KG = 1>
+__global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __restrict__ A,
                                                                 const T* __restrict__ B, int M,
                                                                 int N, int K, QkvEpilogue qe,
                                                                 StoreEpilogue se) {
@@ -113,8 +119,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
   constexpr int STAGE = (BM + BN) * BK;  // elements per LDS stage
   // epilogue staging (bf16 only; fp32 results are stored from registers)
   constexpr int STAGED = sizeof(T) == 2 ? (NT / 64) * (32 * MI) * (32 * NI + 8) : 0;
-  constexpr int SMEM = NSTAGE * STAGE > STAGED ? NSTAGE * STAGE : STAGED;
+  // KG = 2: group 1's accumulators (and NORM sums of squares), fp32, as
+  // [wave][register][lane]
+  constexpr int MERGE = KG > 1 ? (NT / 64) * (MI * NI * 16 + MI) * 64 * 4 / (int)sizeof(T) : 0;
+  constexpr int SMEM1 = KG * NSTAGE * STAGE > STAGED ? KG * NSTAGE * STAGE : STAGED;
+  constexpr int SMEM = SMEM1 > MERGE ? SMEM1 : MERGE;
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 LDS stages");
+  static_assert(KG == 1 || (KG == 2 && !PARTIAL), "K groups: 1, or 2 without split-K partials");
   static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads mismatch");
   static_assert(!QKV || NI == 4, "q/k/v epilogue needs one whole head per wave");
 
@@ -122,7 +133,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int kg = KG > 1 ? (tid >> 6) / (WM * WN) : 0;  // K group
+  const int wave = (tid >> 6) % (WM * WN);             // wave inside its group
   const int wm = wave % WM, wn = wave / WM;
   const int c32 = lane & 31;
   const int hk = lane >> 5;
@@ -143,8 +155,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows vs waves");
   typedef __attribute__((address_space(3))) void lds_void_t;
   typedef __attribute__((address_space(1))) void glb_void_t;
+  T* const gsm = smem + kg * NSTAGE * STAGE;  // this group's stages
   auto gload_lds = [&](int buf, int k0) {
-    char* as = reinterpret_cast<char*>(smem + buf * STAGE);
+    char* as = reinterpret_cast<char*>(gsm + buf * STAGE);
     char* bs = as + BM * BK * sizeof(T);
     const int rsub = lane >> 3, p = lane & 7;
 #pragma unroll
@@ -189,9 +202,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 
   // Split-K (PARTIAL): blockIdx.y picks a K slice of K / gridDim.y; the fp32
   // partial tile goes to se.c as [gridDim.y][M][N].
-  const int KT = K / BK / (PARTIAL ? gridDim.y : 1);
-  if constexpr (PARTIAL) {
-    const size_t koff = (size_t)blockIdx.y * KT * BK;
+  const int KT = K / BK / (PARTIAL ? gridDim.y : KG);
+  if constexpr (PARTIAL || KG > 1) {
+    const size_t koff = (size_t)(PARTIAL ? blockIdx.y : kg) * KT * BK;
     A += koff;
     B += koff;
   }
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
     // The buffer refilled here held tile kt-1, which every wave finished
     // reading before the barrier above.
     if (kt + NSTAGE - 1 < KT) gload_lds((kt + NSTAGE - 1) % NSTAGE, (kt + NSTAGE - 1) * BK);
-    const T* as = smem + buf * STAGE;
+    const T* as = gsm + buf * STAGE;
     const T* bs = as + BM * BK;
     // Fragments are double-buffered in registers: the LDS reads of k-step
     // ks+1 are in flight while the MI*NI MFMAs of step ks run.
@@ -252,6 +265,32 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
     }
   }
   lds_barrier();  // the epilogue reuses the LDS of the last tiles
+  if constexpr (KG > 1) {
+    float* mg = reinterpret_cast<float*>(smem) + (size_t)wave * (MI * NI * 16 + MI) * 64 + lane;
+    if (kg == 1) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mg[((mi * NI + ni) * 16 + i) * 64] = acc[mi][ni][i];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) mg[(MI * NI * 16 + mi) * 64] = ssq[mi];
+    }
+    lds_barrier();  // group 1's sums are in LDS
+    if (kg == 0) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[mi][ni][i] += mg[((mi * NI + ni) * 16 + i) * 64];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) ssq[mi] += mg[(MI * NI * 16 + mi) * 64];
+    }
+    lds_barrier();  // merge reads done before the epilogue stages through the same LDS
+    if (kg == 1) return;
+  }
 
   // ------------------------------------------------------------------ epilogue
   const int row_base = m0 + wm * 32 * MI;
@@ -404,14 +443,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_kernel(const T* __restri
 }
 
 template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false,
-          int NSTAGE = 2, bool NORM = false>
+          int NSTAGE = 2, bool NORM = false, int KG = 1>
 static hipError_t launch_gemm(const T* A, const T* B, int M, int N, int K, const QkvEpilogue& qe,
                               const StoreEpilogue& se, hipStream_t s, int ksplit = 1) {
   constexpr int BM = 32 * MI * WM;
   constexpr int BN = 32 * NI * WN;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV, PARTIAL, NSTAGE, NORM>), dim3(tiles, ksplit),
-                     dim3(WM * WN * 64), 0, s, A, B, M, N, K, qe, se);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, WM, WN, MI, NI, QKV, PARTIAL, NSTAGE, NORM, KG>),
+                     dim3(tiles, ksplit), dim3(WM * WN * 64 * KG), 0, s, A, B, M, N, K, qe, se);
   return hipGetLastError();
 }
 
@@ -555,6 +594,12 @@ __global__ __launch_bounds__(64) void sum_partials_kernel(const float* __restric
 
 constexpr int kCus = 256;
 
+// Two K groups need an even number of 128-byte k-tiles.
+template <typename T>
+static bool k_groups_fit(int K) {
+  return (K / (128 / (int)sizeof(T))) % 2 == 0;
+}
+
 // Tile choice.  Large problems: 256x256 tiles of 8 waves (64x128 each, two
 // waves per SIMD so one wave's MFMAs cover the other's LDS and barrier
 // waits).  Mid-size: 128x128 tiles.  Decode-sized M <= 64: 64x128 tiles.
@@ -619,11 +664,23 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
   if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= kCus / 2)
     return res ? launch_gemm<T, 4, 2, 2, 4, false, false, 2, true>(A, W, M, N, K, qe, se, s)
                : launch_gemm<T, 4, 2, 2, 4, false>(A, W, M, N, K, qe, se, s);
-  if (N % 128 == 0 && ((M + 127) / 128) * (N / 128) >= kCus)
+  // 128x128 tiles of four 64x64 waves.  With exactly one tile per CU (the
+  // 0.6B shape) the K range is split over two wave groups; with more, two
+  // 4-wave workgroups share each CU.
+  const int t128 = ((M + 127) / 128) * (N / 128);
+  if (N % 128 == 0 && t128 >= kCus) {
+    if (t128 == kCus && k_groups_fit<T>(K))
+      return res ? launch_gemm<T, 2, 2, 2, 2, false, false, 2, true, 2>(A, W, M, N, K, qe, se, s)
+                 : launch_gemm<T, 2, 2, 2, 2, false, false, 2, false, 2>(A, W, M, N, K, qe, se, s);
     return res ? launch_gemm<T, 2, 2, 2, 2, false, false, 2, true>(A, W, M, N, K, qe, se, s)
                : launch_gemm<T, 2, 2, 2, 2, false>(A, W, M, N, K, qe, se, s);
+  }
   // Too few 128x128 tiles to fill the chip (e.g. o_proj of a 1024-token
-  // chunk): 64x64 tiles, four 32x32 waves (N is a multiple of 64).
+  // chunk): 64x64 tiles, four 32x32 waves (N is a multiple of 64), the K
+  // range split over two wave groups while there is at most one per CU.
+  if (((M + 63) / 64) * (N / 64) <= kCus && k_groups_fit<T>(K))
+    return res ? launch_gemm<T, 2, 2, 1, 1, false, false, 2, true, 2>(A, W, M, N, K, qe, se, s)
+               : launch_gemm<T, 2, 2, 1, 1, false, false, 2, false, 2>(A, W, M, N, K, qe, se, s);
   return res ? launch_gemm<T, 2, 2, 1, 1, false, false, 2, true>(A, W, M, N, K, qe, se, s)
              : launch_gemm<T, 2, 2, 1, 1, false>(A, W, M, N, K, qe, se, s);
 }

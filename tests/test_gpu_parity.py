@@ -433,6 +433,29 @@ def test_layer_prefill_parity(idx, B, T):
     blk.close()
 
 
+def test_layer_prefill_full_size_0p6b():
+    # The 0.6B shape at full size: o_proj with the residual runs one 128x128
+    # tile per CU, with the K range split over two wave groups.
+    import torch
+    w = WORKLOADS[2]
+    say(f"layer prefill parity full size: {w.name}")
+    inp = prefill_inputs(w)
+    g_in = input_gain(w, w.d, 29)
+    blk = layer_block(inp, w, g_in)
+    x = dev(inp["X"], w.dtype)
+    pos = torch.from_numpy(inp["positions"]).to("cuda")
+    kc = torch.empty((w.B, w.n_kv, w.T, 128), dtype=x.dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    y = host(blk.prefill(x, pos, kc, vc))
+    torch.cuda.synchronize()
+    ref = oracle.prefill_residual(inp["X"], g_in, inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"],
+                                  inp["gq"], inp["gk"], inp["positions"], n_q=w.n_q, n_kv=w.n_kv,
+                                  eps=EPS, theta=ROPE_THETA)
+    assert_close(host(kc), ref["Kc"], w.dtype, "k cache")
+    assert_close(y, ref["Y"], w.dtype, "layer output x + block(norm(x))")
+    blk.close()
+
+
 def test_layer_prefill_full_size_4b_sampled_rows():
     # The 4B shape at full size (T=4096): the q/k/v GEMM with the fused input
     # norm on 256x128 tiles and o_proj with the residual on 256x256 tiles.
