@@ -129,6 +129,11 @@ __device__ __forceinline__ void dma16_to_lds_sv(const void* sbase, uint32_t voff
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
   const uint64_t u = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
+  // M0 (the LDS address) is written inside the statement and declared
+  // clobbered.  Passing it as an input operand ("{m0}") instead let the
+  // compiler drop the wait state it keeps between consecutive statements of
+  // this kind (it cannot see that the load reads M0), and that form faulted
+  // the GPU; it is not used.
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                : : "v"(voff), "s"(u), "s"(lds_base) : "memory", "m0");
 }
