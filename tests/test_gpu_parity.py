@@ -113,6 +113,32 @@ def test_prefill_full_size_sampled_rows(idx):
     assert_close(np.stack([got["Y"][0, t] for t in ts]), ref["Y"], w.dtype, "Y at sampled rows")
 
 
+@pytest.mark.parametrize("n_q,n_kv,B,T", [(8, 4, 2, 4100), (16, 4, 1, 4100)])
+def test_prefill_paired_launch_sampled_rows(n_q, n_kv, B, T):
+    # 520 and 516 query tiles of 128 rows: the paired launch, with an odd
+    # tile count per group (the middle tile runs alone) and a ragged last
+    # tile; n_rep 2 and 4.  Rows at tile edges, the middle tiles and the
+    # ends are checked against the oracle, the caches in full.
+    w = dataclasses.replace(WORKLOADS[2], n_q=n_q, n_kv=n_kv)
+    say(f"prefill parity, paired launch: n_q={n_q} n_kv={n_kv} B={B} T={T}")
+    inp = prefill_inputs(w, B=B, T=T)
+    got = run_prefill_gpu(w, inp, B, T)
+    rep = n_q // n_kv
+    per_tile = 128 // rep                     # tokens per query tile
+    tiles = (T * rep + 127) // 128
+    mid = (tiles // 2) * per_tile
+    ts = sorted({0, 1, per_tile - 1, per_tile, mid - 1, mid, mid + per_tile - 1, mid + per_tile,
+                 T // 3, T - per_tile - 1, T - per_tile, T - 2, T - 1})
+    rows = [(b, t) for b in range(B) for t in ts]
+    ref = oracle.prefill_rows(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], inp["gq"],
+                              inp["gk"], inp["positions"], rows, n_q=n_q, n_kv=n_kv, eps=EPS,
+                              theta=ROPE_THETA)
+    for b in range(B):
+        assert_close(got["Kc"][b][:, :T], ref["Kc"][b], w.dtype, f"k cache (all tokens, seq {b})")
+        assert_close(got["Vc"][b][:, :T], ref["Vc"][b], w.dtype, f"v cache (all tokens, seq {b})")
+    assert_close(np.stack([got["Y"][b, t] for b, t in rows]), ref["Y"], w.dtype, "Y at sampled rows")
+
+
 def test_prefill_mha_case():
     # n_kv == n_q: standard multi-head attention (n_rep = 1).
     w = dataclasses.replace(WORKLOADS[2], n_q=8, n_kv=8)
