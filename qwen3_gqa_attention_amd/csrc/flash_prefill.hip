@@ -16,12 +16,7 @@
 // merged at the end (the same log-sum-exp merge as split-K decode).  The two
 // waves that share a SIMD thus work on the same query tile for its whole
 // duration, which halves its critical path.  Workgroups are issued heaviest
-// (longest key range) first.  Paired launch (a first prefill of equal-length
-// sequences with 512..1023 query tiles, e.g. two 2048-token sequences of
-// the 0.6B shape): each workgroup takes query tile T-1-p and its light
-// partner p of the same group; key half 1 runs the light tile's key tiles
-// first, stores its rows, and then takes the heavy tile's last key tiles, so
-// every workgroup has about the same work and the chip runs one round.
+// (longest key range) first.
 //
 // Per wave and 64-key tile (bf16):
 //   S^T[key, q] = K . Q^T    -- A = K rows from LDS, B = Q^T held in VGPRs;
@@ -68,7 +63,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             int n_q, int n_kv, KvAddr kv,
                                                             const int32_t* __restrict__ past,
                                                             int window, int nsplit,
-                                                            float* __restrict__ part, int paired) {
+                                                            float* __restrict__ part) {
   using MF = Mfma32<T>;
   constexpr int BN = FlashTile<T>::BN;
   constexpr int NKB = BN / 32;                 // 32-key blocks per tile
@@ -106,11 +101,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int rest = blockIdx.x / groups;
   const int split = rest % nsplit;
   // Query tiles are issued heaviest (longest key range) first, so lighter
-  // ones fill CUs as they free up.  Paired launch: workgroup p of a group
-  // takes query tile tiles_per_group - 1 - p (heavy) and tile p (light,
-  // if it is a different tile).
+  // ones fill CUs as they free up.
   const int qt = tiles_per_group - 1 - rest / nsplit;
-  const int qt_l = paired && rest < qt ? rest : -1;
   const int b = bg / n_kv, g = bg % n_kv;
   // Token rows of sequence b: q0 .. q0 + Tb - 1 (a variable-length batch
   // gives them in cu_seqlens; else every sequence has T_len).  Query tiles
@@ -132,33 +124,24 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int th = tid & 255;                    // thread index inside the key half
   const int c32 = lane & 31, hk = lane >> 5;
 
-  // This wave's rows of query tile `qtile` (the light tile first in key
-  // half 1 of a paired workgroup, then the heavy one).
-  int Rw, Rl, qtok, tok, head, w_tok_lo, w_tok_hi, key_lo, w_key_lo, w_mask_lo;
-  bool row_ok, wave_active;
-  auto set_ctx = [&](int qtile) {
-    Rw = qtile * 128 + qblk * 32;
-    Rl = Rw + c32;
-    row_ok = Rl < rows_total;
-    qtok = row_ok ? Rl / n_rep : Tb - 1;      // token inside the chunk
-    tok = P + qtok;                           // its key position
-    head = g * n_rep + (row_ok ? Rl % n_rep : 0);
-    wave_active = Rw < rows_total;
-    w_tok_lo = P + min(Rw, rows_total - 1) / n_rep;
-    w_tok_hi = P + min(Rw + 31, rows_total - 1) / n_rep;
-    // Sliding window W (0: none): key position j is visible to the token at
-    // key position i iff i - W < j <= i.  key_lo is this lane's first
-    // visible key; keys below w_mask_lo are masked for at least one row of
-    // the wave.
-    key_lo = window > 0 ? tok - window + 1 : 0;
-    w_key_lo = window > 0 ? w_tok_lo - window + 1 : 0;
-    w_mask_lo = window > 0 ? w_tok_hi - window + 1 : 0;
-  };
-  const int nl_tiles = qt_l >= 0 ? (P + min(qt_l * 128 + 127, rows_total - 1) / n_rep) / BN + 1 : 0;
-  set_ctx(KSPLIT == 2 && kh == 1 && nl_tiles > 0 ? qt_l : qt);
+  const int R0 = qt * 128;
+  const int Rw = R0 + qblk * 32;
+  const int Rl = Rw + c32;
+  const bool row_ok = Rl < rows_total;
+  const int qtok = row_ok ? Rl / n_rep : Tb - 1;      // token inside the chunk
+  const int tok = P + qtok;                            // its key position
+  const int head = g * n_rep + (row_ok ? Rl % n_rep : 0);
+  const bool wave_active = Rw < rows_total;
+  const int w_tok_lo = P + min(Rw, rows_total - 1) / n_rep;
+  const int w_tok_hi = P + min(Rw + 31, rows_total - 1) / n_rep;
+  // Sliding window W (0: none): key position j is visible to the token at
+  // key position i iff i - W < j <= i.  key_lo is this lane's first visible
+  // key; keys below w_mask_lo are masked for at least one row of the wave.
+  const int key_lo = window > 0 ? tok - window + 1 : 0;
+  const int w_key_lo = window > 0 ? w_tok_lo - window + 1 : 0;
+  const int w_mask_lo = window > 0 ? w_tok_hi - window + 1 : 0;
   // Key tiles of the workgroup: from the first key its first row sees to the
   // last key its last row sees.
-  const int R0 = qt * 128;
   const int kmax = P + min(R0 + 127, rows_total - 1) / n_rep;
   const int kmin = window > 0 ? max(0, P + R0 / n_rep - window + 1) : 0;
   const int tl0 = kmin / BN;
@@ -170,12 +153,11 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
 
   // Q^T fragments for the whole d_head, kept in VGPRs.
   typename MF::frag qf[DSTEPS];
-  auto load_q = [&]() {
+  {
     const T* qrow = Q + ((size_t)(q0 + qtok) * n_q + head) * kHeadDim + hk * MF::KL;
 #pragma unroll
     for (int ks = 0; ks < DSTEPS; ++ks) qf[ks] = row_ok ? MF::load(qrow + ks * MF::K) : MF::zero();
-  };
-  load_q();
+  }
 
   // Each key tile lies inside one cache block (paged block sizes are powers
   // of two >= 64), so one row lookup per tile addresses all its rows.
@@ -462,61 +444,15 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     }
   };
 
-  // O / l of this lane's row (the current query tile), rounded to T.
-  auto store_out = [&]() {
-    const float inv = 1.f / l_run;
-    T* orow = Out + ((size_t)(q0 + qtok) * n_q + head) * kHeadDim;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = db * 32 + 8 * i4 + 4 * hk;
-        if constexpr (VT) {
-          u32x2_v w{pack_bf16x2(o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv),
-                    pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv)};
-          *reinterpret_cast<u32x2_v*>(orow + d) = w;
-        } else {
-          f32x4_v w{o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv, o[db][i4 * 4 + 2] * inv,
-                    o[db][i4 * 4 + 3] * inv};
-          *reinterpret_cast<f32x4_v*>(orow + d) = w;
-        }
-      }
-  };
-  // Key half 1 of a paired workgroup after the light tile's last key tile:
-  // its rows are complete (this half saw all their keys), so they are
-  // normalised and stored; then the running state restarts for the heavy
-  // tile's rows, whose Q fragments are loaded.
-  auto switch_to_heavy = [&]() {
-    const float lsum = l_run + __shfl_xor(l_run, 32, kWave);
-    if (row_ok) {
-      l_run = lsum;
-      store_out();
-    }
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = f32x16_v{};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mbias[i] = 0.f;
-    set_ctx(qt);
-    load_q();
-  };
-
   // Key halves: half 0 takes tiles [0, n0), half 1 tiles [n0, ntiles).  Each
   // half has two LDS stages (kh*2, kh*2+1) fed from two register sets: tile
   // i+2's global loads are issued while tile i runs, and tile i+1 (loaded one
   // iteration earlier) is staged after it.  Both halves run n0 iterations so
   // every wave meets every barrier.
   // (uniform; read from the first lane so the loop control stays scalar)
-  // Paired (key half 1 also runs the light tile's nl key tiles, first): the
-  // heavy tile's split point moves so that both halves get half of the
-  // nh + nl tiles.
-  const int nl = __builtin_amdgcn_readfirstlane(KSPLIT == 2 ? nl_tiles : 0);
-  const int n0 = __builtin_amdgcn_readfirstlane(KSPLIT == 2 ? (ntiles + nl + 1) / 2 : ntiles);
+  const int n0 = __builtin_amdgcn_readfirstlane(KSPLIT == 2 ? (ntiles + 1) / 2 : ntiles);
   const int base = __builtin_amdgcn_readfirstlane(t_lo + (kh ? n0 : 0));
-  const int cnt = __builtin_amdgcn_readfirstlane(kh ? ntiles + nl - n0 : n0);
-  // key tile of step i of this half (key tiles of the light tile start at 0)
-  auto tile_at = [&](int i) { return kh && i < nl ? i : base + i - (kh ? nl : 0); };
+  const int cnt = __builtin_amdgcn_readfirstlane(kh ? ntiles - n0 : n0);
   const int s0 = kh * 2, s1 = kh * 2 + 1;
   if constexpr (VT) {
     // Two LDS stages per key half: tile i+1's loads are issued before tile i
@@ -527,20 +463,18 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     // stage i % 2 of the half.
     auto step = [&](int i, auto stage) {
       constexpr int P = decltype(stage)::value;
-      if (kh && nl > 0 && i == nl) switch_to_heavy();
-      if (i + 1 < cnt) dma_tile(tile_at(i + 1), P ? s0 : s1);
-      if (i < cnt) tile(tile_at(i), stage);
+      if (i + 1 < cnt) dma_tile(base + i + 1, P ? s0 : s1);
+      if (i < cnt) tile(base + i, stage);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i+1 has landed
       lds_barrier();
     };
-    if (cnt > 0) dma_tile(tile_at(0), s0);
+    if (cnt > 0) dma_tile(base, s0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and tile 0
     lds_barrier();
     for (int i = 0; i < n0; i += 2) {
       step(i, std::integral_constant<int, 0>{});
       if (i + 1 < n0) step(i + 1, std::integral_constant<int, 1>{});
     }
-    if (kh && nl > 0 && nl >= n0) switch_to_heavy();
   } else {
     for (int i = 0; i < n0; ++i) {
       if (i < cnt) {
@@ -602,7 +536,23 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     }
     return;
   }
-  store_out();
+  const float inv = 1.f / l_run;
+  T* orow = Out + ((size_t)(q0 + qtok) * n_q + head) * kHeadDim;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = db * 32 + 8 * i4 + 4 * hk;
+      if constexpr (VT) {
+        u32x2_v w{pack_bf16x2(o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv),
+                  pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv)};
+        *reinterpret_cast<u32x2_v*>(orow + d) = w;
+      } else {
+        f32x4_v w{o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv, o[db][i4 * 4 + 2] * inv,
+                  o[db][i4 * 4 + 3] * inv};
+        *reinterpret_cast<f32x4_v*>(orow + d) = w;
+      }
+    }
 }
 
 // Merge the nsplit partial results of each (token, query head): one online
@@ -663,22 +613,13 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
   // Few workgroups: split each query tile's key range over two wave groups
   // so both waves of a SIMD serve the same tile.  Many: 4-wave workgroups,
   // two resident per CU.
-  const int qwgs = flash_query_wgs(B, T_len, n_q, n_kv);
-  // Paired launch (bf16, a first prefill of equal-length sequences, no
-  // window, 512..1023 query tiles): one workgroup per heavy / light pair of
-  // query tiles of the same group, so every workgroup has about the same
-  // number of key tiles and the chip runs one round of workgroups.
-  const bool paired = sizeof(T) == 2 && nsplit == 1 && !cu_seqlens && !past && window == 0 &&
-                      qwgs >= 2 * 256 && qwgs < 4 * 256;
-  const int tpg = (T_len * (n_q / n_kv) + 127) / 128;
-  const int wgs = paired ? B * n_kv * ((tpg + 1) / 2) : qwgs * nsplit;
-  if (paired || wgs < 4 * 256)
+  const int wgs = flash_query_wgs(B, T_len, n_q, n_kv) * nsplit;
+  if (wgs < 4 * 256)
     hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part,
-                       paired ? 1 : 0);
+                       T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part);
   else
     hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part, 0);
+                       T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part);
   if (nsplit > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -114,13 +114,13 @@ def test_prefill_full_size_sampled_rows(idx):
 
 
 @pytest.mark.parametrize("n_q,n_kv,B,T", [(8, 4, 2, 4100), (16, 4, 1, 4100)])
-def test_prefill_paired_launch_sampled_rows(n_q, n_kv, B, T):
-    # 520 and 516 query tiles of 128 rows: the paired launch, with an odd
-    # tile count per group (the middle tile runs alone) and a ragged last
-    # tile; n_rep 2 and 4.  Rows at tile edges, the middle tiles and the
-    # ends are checked against the oracle, the caches in full.
+def test_prefill_long_odd_tile_count_sampled_rows(n_q, n_kv, B, T):
+    # 520 and 516 query tiles of 128 rows (two rounds of 8-wave workgroups),
+    # an odd tile count per KV group and a ragged last tile; n_rep 2 and 4.
+    # Rows at tile edges, the middle tiles and the ends are checked against
+    # the oracle, the caches in full.
     w = dataclasses.replace(WORKLOADS[2], n_q=n_q, n_kv=n_kv)
-    say(f"prefill parity, paired launch: n_q={n_q} n_kv={n_kv} B={B} T={T}")
+    say(f"prefill parity, long odd tile count: n_q={n_q} n_kv={n_kv} B={B} T={T}")
     inp = prefill_inputs(w, B=B, T=T)
     got = run_prefill_gpu(w, inp, B, T)
     rep = n_q // n_kv
