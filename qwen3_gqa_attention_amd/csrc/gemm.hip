@@ -461,14 +461,18 @@ static hipError_t launch_gemm(const T* A, const T* B, int M, int N, int K, const
 // ---------------------------------------------------------------------------
 constexpr int kSmallM = 64;
 
-// Number of K slices for a decode projection: about 256 workgroups, each
-// slice a whole number of 128-byte k-tiles.
+// Number of K slices for a decode projection: the fewest (a power of two,
+// each slice a whole number of 128-byte k-tiles) that give at least 64
+// workgroups.  More slices spread the weight stream over more CUs but write
+// and re-read more fp32 partials: at 64 rows, 64 workgroups measured fastest
+// (0.6B q/k/v 11.2 -> 10.5 us with 2 slices instead of 8; o_proj 10.3 ->
+// 7.7 us with 8 instead of 32, partial GEMM plus its finishing kernel).
 template <typename T>
 static int small_m_ksplit(int N, int K) {
   constexpr int BK = 128 / sizeof(T);
   const int tiles = N / 128;
   int ks = 1;
-  while (tiles * ks * 2 <= 256 && (K / BK) % (ks * 2) == 0) ks *= 2;
+  while (tiles * ks < 64 && (K / BK) % (ks * 2) == 0) ks *= 2;
   return ks;
 }
 

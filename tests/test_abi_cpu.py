@@ -92,9 +92,10 @@ def test_workspace_size_prefill_and_decode(built_lib):
     cap, N = 32832, 64
     nchunk = -(-cap // 512)
     slots = N * 8 * nchunk * 2
-    # split-K partials of the 64-row projections: q/k/v 8 slices x 64 x 4096,
-    # o_proj 32 slices x 64 x 1024 (fp32); the larger is reserved
-    part = max(8 * 64 * 4096, 32 * 64 * 1024) * 4
+    # split-K partials of the 64-row projections (the fewest K slices giving
+    # at least 64 workgroups of 128 columns): q/k/v 2 slices x 64 x 4096,
+    # o_proj 8 slices x 64 x 1024 (fp32); the larger is reserved
+    part = max(2 * 64 * 4096, 8 * 64 * 1024) * 4
     want = 2 * align(N * 2048 * 2) + align(slots * 128 * 4) + align(slots * 2 * 4) + align(part)
     assert q3.qwen3_attn_workspace_size(d, 1, N, 1, cap) == want
 
