@@ -7,8 +7,10 @@
 //
 // Workgroup tile BM x BN x BK (BK = 128 bytes of K per row), WM x WN waves,
 // each wave owning (32*MI) x (32*NI) outputs as MI x NI accumulators of the
-// 32x32 MFMA.  Large wave tiles keep LDS traffic per MFMA low: a 128x128 wave
-// tile reads 8 fragments (8 KB) from LDS per 16 MFMAs.
+// 32x32 MFMA.  Large wave tiles keep LDS traffic per MFMA low: the 64x128
+// wave tile of the q/k/v GEMM reads 6 fragments (6 KB) from LDS per 8 MFMAs.
+// When a projection has only one tile per CU, KG = 2 gives the tile two
+// groups of waves that each run half of K (see gemm_nt_kernel).
 //
 // For the q/k/v projection NI = 4: a wave's 128 columns are exactly one head
 // of d_head = 128, so the epilogue sees whole heads.  With the 32x32
