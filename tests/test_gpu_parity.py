@@ -388,6 +388,21 @@ def test_decode_parity_ragged(dtype, n_q, n_kv):
     check_decode(w, inp, kc, vc, got)
 
 
+@pytest.mark.parametrize("N", [1, 64, 65])
+def test_decode_batch_sizes_at_the_projection_path_edges(N):
+    # N <= 64 runs the projections split-K (one 64-row tile, ragged for N < 64);
+    # N = 65 is the smallest batch on the tiled path (a one-row second tile).
+    w = WORKLOADS[5]
+    say(f"decode batch-size edge: N={N}")
+    lens = np.random.default_rng(100 + N).integers(0, 600, size=N).astype(np.int32)
+    inp = decode_inputs(w, N=N)
+    inp["positions"] = lens
+    cap = 640
+    kc, vc = decode_cache_host(w, lens, cap)
+    got = run_decode_gpu(w, inp, kc, vc, cap)
+    check_decode(w, inp, kc, vc, got)
+
+
 def test_decode_full_size_sampled_sequences():
     # 64 sequences with caches of 1024..32768 tokens (several GB); the caches
     # are drawn on the device with torch's seeded generator, sampled
