@@ -297,7 +297,7 @@ class Qwen3Attention:
         nbytes = self.workspace_size(False, B, T)
         ws = self._workspace(nbytes, workspace)
         st = qwen3_attn_forward_prefill(
-            self.handle, _ptr(hidden, "hidden", self.dtype), _ptr(positions, "positions", torch.int32, (B, T)),
+            self.handle, _ptr(hidden, "hidden", self.dtype, (B, T, self.d_model)), _ptr(positions, "positions", torch.int32, (B, T)),
             _ptr(k_cache, "k_cache", self.dtype, (B, self.n_kv, cap, self.d_head)),
             _ptr(v_cache, "v_cache", self.dtype, (B, self.n_kv, cap, self.d_head)), cap,
             _ptr(out, "out", self.dtype, (B, T, d)), B, T, _ptr(ws, "workspace"), ws.numel() * ws.element_size(),
@@ -318,7 +318,7 @@ class Qwen3Attention:
         nbytes = self.workspace_size(False, B, T)
         ws = self._workspace(nbytes, workspace)
         st = qwen3_attn_forward_prefill_chunk(
-            self.handle, _ptr(hidden, "hidden", self.dtype), _ptr(positions, "positions", torch.int32, (B, T)),
+            self.handle, _ptr(hidden, "hidden", self.dtype, (B, T, self.d_model)), _ptr(positions, "positions", torch.int32, (B, T)),
             _ptr(past_len, "past_len", torch.int32, (B,)),
             _ptr(k_cache, "k_cache", self.dtype, (B, self.n_kv, cap, self.d_head)),
             _ptr(v_cache, "v_cache", self.dtype, (B, self.n_kv, cap, self.d_head)), cap,
@@ -340,7 +340,7 @@ class Qwen3Attention:
             out = torch.empty_like(hidden)
         ws = self._workspace(self.workspace_size(False, B, T), workspace)
         st = qwen3_attn_forward_prefill_paged(
-            self.handle, _ptr(hidden, "hidden", self.dtype), _ptr(positions, "positions", torch.int32, (B, T)),
+            self.handle, _ptr(hidden, "hidden", self.dtype, (B, T, self.d_model)), _ptr(positions, "positions", torch.int32, (B, T)),
             None if past_len is None else _ptr(past_len, "past_len", torch.int32, (B,)),
             _ptr(block_table, "block_table", torch.int32, (B, mb)), mb,
             _ptr(k_pool, "k_pool", self.dtype, (nb, self.n_kv, bs, self.d_head)),
@@ -368,7 +368,7 @@ class Qwen3Attention:
         kshape = (n0, self.n_kv, s2, self.d_head)
         mb = 0 if block_table is None else block_table.shape[1]
         st = qwen3_attn_forward_prefill_varlen(
-            self.handle, _ptr(hidden, "hidden", self.dtype),
+            self.handle, _ptr(hidden, "hidden", self.dtype, (total, self.d_model)),
             _ptr(positions, "positions", torch.int32, (total,)),
             _ptr(cu_seqlens, "cu_seqlens", torch.int32, (B + 1,)),
             None if past_len is None else _ptr(past_len, "past_len", torch.int32, (B,)),
@@ -393,7 +393,7 @@ class Qwen3Attention:
             out = torch.empty_like(hidden)
         ws = self._workspace(self.workspace_size(True, N, 1, mb * bs), workspace)
         st = qwen3_attn_forward_decode_paged(
-            self.handle, _ptr(hidden, "hidden", self.dtype), _ptr(positions, "positions", torch.int32, (N,)),
+            self.handle, _ptr(hidden, "hidden", self.dtype, (N, self.d_model)), _ptr(positions, "positions", torch.int32, (N,)),
             _ptr(block_table, "block_table", torch.int32, (N, mb)), mb,
             _ptr(k_pool, "k_pool", self.dtype, (nb, self.n_kv, bs, self.d_head)),
             _ptr(v_pool, "v_pool", self.dtype, (nb, self.n_kv, bs, self.d_head)), bs,
@@ -413,7 +413,7 @@ class Qwen3Attention:
         nbytes = self.workspace_size(True, N, 1, cap)
         ws = self._workspace(nbytes, workspace)
         st = qwen3_attn_forward_decode(
-            self.handle, _ptr(hidden, "hidden", self.dtype), _ptr(positions, "positions", torch.int32, (N,)),
+            self.handle, _ptr(hidden, "hidden", self.dtype, (N, self.d_model)), _ptr(positions, "positions", torch.int32, (N,)),
             _ptr(k_cache, "k_cache", self.dtype, (N, self.n_kv, cap, self.d_head)),
             _ptr(v_cache, "v_cache", self.dtype, (N, self.n_kv, cap, self.d_head)), cap,
             _ptr(out, "out", self.dtype, (N, d)), N, _ptr(ws, "workspace"), ws.numel() * ws.element_size(),

@@ -719,6 +719,14 @@ def test_forward_argument_errors():
     assert f(blk.handle, None, P(pos), P(kc), P(kc), 16, P(out), 1, 8, P(ws), need, s) == 1
     assert f(blk.handle, P(x), P(pos), P(kc), P(kc), 16, P(out), 1, 8, P(ws), need, s) == 0
     torch.cuda.synchronize()
+    # the binding checks hidden's width against the handle's d_model (the C ABI cannot)
+    x_narrow = x[..., : w.d // 2].contiguous()
+    with pytest.raises(ValueError):
+        blk.prefill(x_narrow, pos, kc, kc.clone())
+    with pytest.raises(ValueError):
+        blk.decode(x_narrow[0], torch.zeros(8, dtype=torch.int32, device="cuda"),
+                   torch.zeros((8, w.n_kv, 16, 128), dtype=x.dtype, device="cuda"),
+                   torch.zeros((8, w.n_kv, 16, 128), dtype=x.dtype, device="cuda"))
     blk.close()
     # decode with an n_rep the decode kernel does not instantiate
     w7 = dataclasses.replace(w, n_q=14, n_kv=2)
