@@ -642,6 +642,12 @@ hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const
   if (t128 >= kCus)  // 256x128 tiles of eight 32x128 waves
     return norm ? launch_gemm<T, 8, 1, 1, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
                 : launch_gemm<T, 8, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
+  // 128x128 tiles of four 32x128 waves.  At most one per CU (e.g. a
+  // 1024-token chunk: 256 tiles): the K range is split over two wave groups,
+  // so eight waves keep loads in flight instead of four.
+  if (((M + 127) / 128) * (N / 128) <= kCus && k_groups_fit<T>(K))
+    return norm ? launch_gemm<T, 4, 1, 1, 4, true, false, 2, true, 2>(X, Wqkv, M, N, K, e, se, s)
+                : launch_gemm<T, 4, 1, 1, 4, true, false, 2, false, 2>(X, Wqkv, M, N, K, e, se, s);
   return norm ? launch_gemm<T, 4, 1, 1, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
               : launch_gemm<T, 4, 1, 1, 4, true>(X, Wqkv, M, N, K, e, se, s);
 }
