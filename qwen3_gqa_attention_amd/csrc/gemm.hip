@@ -345,11 +345,37 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
     }
   }
   int head = 0, kind = 3;  // kind 3: plain projection output
+  // 256x256 q/k/v tiles: the two waves of a row block share the RoPE angles
+  constexpr bool kShareAngles = QKV && WN == 2 && KG == 1;
+  const bool share = kShareAngles && (n0 >> 7) < qe.n_q + qe.n_kv;
+  static_assert(!kShareAngles || WM * MI * 16 * 64 * 16 <= SMEM * (int)sizeof(T), "angles do not fit");
   if constexpr (QKV) {
     // This wave's 128 columns are head (n0/128 + wn): [0, n_q) query heads,
     // then n_kv key heads, then n_kv value heads.
     head = (n0 >> 7) + wn;
     kind = head < qe.n_q ? 0 : (head < qe.n_q + qe.n_kv ? 1 : 2);
+    if constexpr (kShareAngles) {
+      // The tile's two waves of a row block need the same (row, frequency)
+      // angles: wave wn evaluates frequency c32 + 32*wn for all its rows and
+      // the pair swaps them through LDS, halving the sin/cos work.  Every
+      // wave of the workgroup takes part when the tile's first head is a
+      // query or key head (a value-head wave next to a key head included).
+      if (share) {
+        const int f = c32 + 32 * wn;
+        const float wh = qe.rope_rev[f], wl = qe.rope_rev[64 + f];
+        float* ang = reinterpret_cast<float*>(smem) + ((size_t)wm * MI * 16 * 64 + lane) * 4 + 2 * wn;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
+            float sn, cn;
+            rope_sincos(qe.positions[row], wh, wl, &sn, &cn);
+            *reinterpret_cast<float2*>(ang + (mi * 16 + i) * 64 * 4) = make_float2(cn, sn);
+          }
+        lds_barrier();  // both frequencies of every row are in LDS
+      }
+    }
     if (kind != 2) {
       float gain[4];
       const T* g = reinterpret_cast<const T*>(kind == 0 ? qe.gq : qe.gk);
@@ -362,12 +388,22 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         float2 cs0[16], cs1[16];
+        if constexpr (kShareAngles) {  // kind != 2 implies share here
+          const float4* ang4 = reinterpret_cast<const float4*>(smem) + (wm * MI + mi) * 16 * 64 + lane;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
-          const int pos = qe.positions[row];
-          rope_sincos(pos, w0h, w0l, &cs0[i].y, &cs0[i].x);
-          rope_sincos(pos, w1h, w1l, &cs1[i].y, &cs1[i].x);
+          for (int i = 0; i < 16; ++i) {
+            const float4 a = ang4[i * 64];
+            cs0[i] = make_float2(a.x, a.y);
+            cs1[i] = make_float2(a.z, a.w);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
+            const int pos = qe.positions[row];
+            rope_sincos(pos, w0h, w0l, &cs0[i].y, &cs0[i].x);
+            rope_sincos(pos, w1h, w1l, &cs1[i].y, &cs1[i].x);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -404,6 +440,7 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
     }
   };
 
+  if (kShareAngles && share) lds_barrier();  // angle reads done before the staging writes
   if constexpr (sizeof(T) == 2) {
     // Stage the wave's (32*MI) x (32*NI) bf16 block in LDS (rows padded by 16
     // bytes), then write whole 16-byte pieces of rows to global memory.
