@@ -83,9 +83,11 @@ def test_prefill_parity(idx, B, T):
     assert_close(got["Y"], ref["Y"], w.dtype, "block output Y")
 
 
-def test_prefill_full_size_0p6b():
-    # The benchmark's workload, compared in full.
-    w = WORKLOADS[2]
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_full_size_0p6b(dtype):
+    # The benchmark's workload, compared in full; in fp32 too, which takes the
+    # same 256x256 q/k/v tiles (shared RoPE angles) through the fp32 MFMAs.
+    w = dataclasses.replace(WORKLOADS[2], dtype=dtype)
     say(f"prefill parity full size: {w.name}")
     inp = prefill_inputs(w)
     got = run_prefill_gpu(w, inp, w.B, w.T)
@@ -113,12 +115,15 @@ def test_prefill_full_size_sampled_rows(idx):
     assert_close(np.stack([got["Y"][0, t] for t in ts]), ref["Y"], w.dtype, "Y at sampled rows")
 
 
-@pytest.mark.parametrize("n_q,n_kv,B,T", [(8, 4, 2, 4100), (16, 4, 1, 4100)])
+@pytest.mark.parametrize("n_q,n_kv,B,T", [(8, 4, 2, 4100), (16, 4, 1, 4100), (6, 3, 1, 11008)])
 def test_prefill_long_odd_tile_count_sampled_rows(n_q, n_kv, B, T):
     # 520 and 516 query tiles of 128 rows (two rounds of 8-wave workgroups),
     # an odd tile count per KV group and a ragged last tile; n_rep 2 and 4.
     # Rows at tile edges, the middle tiles and the ends are checked against
-    # the oracle, the caches in full.
+    # the oracle, the caches in full.  With 6/3 heads the q/k/v GEMM runs
+    # 256x256 tiles (two heads each) and one tile pairs the last key head with
+    # the first value head, so a value-head wave evaluates half of the key
+    # head's RoPE angles.
     w = dataclasses.replace(WORKLOADS[2], n_q=n_q, n_kv=n_kv)
     say(f"prefill parity, long odd tile count: n_q={n_q} n_kv={n_kv} B={B} T={T}")
     inp = prefill_inputs(w, B=B, T=T)
