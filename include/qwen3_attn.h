@@ -30,6 +30,10 @@
  *     surface at the caller's next synchronisation of the stream.
  *   - The forward calls allocate nothing; scratch memory is the caller's
  *     workspace.  Two calls in flight at once need two workspaces.
+ *   - A handle's weights never change after create.  Its one mutable part is
+ *     the optional stage timing (qwen3_attn_enable_stage_timing): while it is
+ *     on, each forward call records events into the handle, so calls on one
+ *     handle must then not overlap (from several host threads or streams).
  */
 #ifndef QWEN3_ATTN_H
 #define QWEN3_ATTN_H
@@ -58,8 +62,10 @@ typedef enum {
 } qwen3_attn_status;
 
 /* Block configuration.  Supported: d_head == 128; n_q % n_kv == 0;
- * d_model % 128 == 0; n_q / n_kv <= 16 for decode; eps >= 0; rope_theta > 1;
- * sliding_window >= 0. */
+ * d_model % 128 == 0; eps >= 0; rope_theta > 1; sliding_window >= 0.
+ * The decode calls also need n_q / n_kv in {1, 2, 3, 4, 5, 6, 8, 16}
+ * (they return EUNSUPPORTED for any other group size; the prefill calls take
+ * every n_q / n_kv). */
 typedef struct {
   int32_t d_model;   /* hidden size d */
   int32_t n_q;       /* query heads */
@@ -95,8 +101,9 @@ typedef struct {
  * EUNSUPPORTED before any HIP call), then allocates handle-owned device
  * memory and copies the weights into it on `stream` (q/k/v merged into one
  * [(n_q+2*n_kv)*d_head, d_model] matrix).  The caller may free its weight
- * buffers once `stream` has completed.  The handle is immutable afterwards.
- * On error *out is set to NULL. */
+ * buffers once `stream` has completed.  The weights are immutable
+ * afterwards (only the stage-timing state below changes).  On error *out is
+ * set to NULL. */
 qwen3_attn_status qwen3_attn_create(const qwen3_attn_desc* desc,
                                     const qwen3_attn_weights* weights,
                                     void* stream, qwen3_attn_t** out);
@@ -127,7 +134,12 @@ qwen3_attn_status qwen3_attn_create_with_input_norm(const qwen3_attn_desc* desc,
 size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
                                  int32_t B_or_N, int32_t T, int64_t cache_cap);
 
-/* Prefill: B sequences of T new tokens each, over EMPTY caches.
+/* Prefill: B sequences of T new tokens each, over EMPTY caches
+ * ("Assembling a large model from scratch", section "The complete code": the
+ * Attention forward with an empty KVCache, so S = T keys and the mask
+ * tril(diagonal = S - T) is the plain causal one; the block's steps in the
+ * order of "Qwen3 Architecture Layer-by-Layer", section "Layer 3 -
+ * Qwen3Attention": projections, q_norm / k_norm, RoPE, attention, o_proj).
  *   hidden    [B, T, d_model]
  *   positions [B, T] int32, drives RoPE only (the mask is by token index:
  *             token t sees cache slots 0..t)
@@ -263,7 +275,11 @@ qwen3_attn_status qwen3_attn_forward_decode_paged(qwen3_attn_t* h, const void* h
                                                   void* workspace, size_t workspace_bytes,
                                                   void* stream);
 
-/* Decode: one new token for each of N sequences.
+/* Decode: one new token for each of N sequences ("Assembling a large model
+ * from scratch", section "The complete code": KVCache.update appends the new
+ * key and value after the L cached ones, and the mask tril(diagonal = S - T)
+ * with T = 1, S = L + 1 lets the new token see every key, its own included;
+ * the generate loop calls this once per new token).
  *   hidden    [N, d_model]
  *   positions [N] int32 device array, positions[s] = L_s = the number of
  *             tokens already cached for sequence s (0 allowed).  Precondition
@@ -287,8 +303,9 @@ void qwen3_attn_destroy(qwen3_attn_t* h);
 /* Measurement aid.  With capacity > 0, each later forward call on this handle
  * records a HIP event on its stream before each of its three kernels
  * (q/k/v projection, attention, o_proj) and one after the last, for up to
- * `capacity` calls; capacity 0 turns it off.  Not thread-safe; the handle's
- * results are unaffected. */
+ * `capacity` calls; capacity 0 turns it off.  This is the handle's only
+ * mutable state: while timing is on, forward calls on the handle must not
+ * overlap (not thread-safe).  The handle's results are unaffected. */
 qwen3_attn_status qwen3_attn_enable_stage_timing(qwen3_attn_t* h, int32_t capacity);
 
 /* Waits for the last recorded call, then returns in ms[0..2] the summed

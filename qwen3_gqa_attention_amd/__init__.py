@@ -251,7 +251,9 @@ class Qwen3Attention:
             name = "qwen3_attn_create_with_input_norm"
         if st != 0:
             raise Qwen3AttnError(name, st)
-        self._ws = None
+        # Workspaces the calls allocate when the caller passes none, one per
+        # stream (two calls in flight on different streams need two).
+        self._ws = {}
 
     def close(self):
         if getattr(self, "handle", 0):
@@ -280,12 +282,19 @@ class Qwen3Attention:
         return qwen3_attn_workspace_size(self.desc, int(is_decode), B_or_N, T, cache_cap)
 
     def _workspace(self, nbytes: int, workspace):
+        """The caller's workspace, or this object's own one for the current
+        stream.  Each stream gets its own buffer, allocated while that stream
+        is current, so torch's allocator orders its reuse after the stream's
+        earlier calls; growing it on the same stream is therefore safe too."""
         torch = _torch()
         if workspace is not None:
             return workspace
-        if self._ws is None or self._ws.numel() < nbytes:
-            self._ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-        return self._ws
+        key = torch.cuda.current_stream().cuda_stream
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+            self._ws[key] = ws
+        return ws
 
     def prefill(self, hidden, positions, k_cache, v_cache, out=None, workspace=None):
         """hidden [B,T,d]; positions [B,T] int32; caches [B,n_kv,cap,128] (written)."""

@@ -106,21 +106,26 @@ __device__ __forceinline__ u32x4_v ld16(const void* p) { return *reinterpret_cas
 __device__ __forceinline__ void st16(void* p, u32x4_v v) { *reinterpret_cast<u32x4_v*>(p) = v; }
 
 // 16-byte direct global -> LDS load (global_load_lds_dwordx4): lane i of the
-// wave writes the 16 bytes at `g` to LDS byte address lds_base + 16 * i
-// (lds_base must be wave-uniform).  Written as inline asm so that the
-// compiler does not treat it as a pending write to all of LDS: it would
-// otherwise make every later LDS read it cannot disambiguate (the
-// transposing reads, for instance) wait for the load.  The instruction has
-// no result register; completion is tracked by vmcnt, so the caller waits
-// with s_waitcnt vmcnt before a barrier that publishes the data.
-__device__ __forceinline__ void dma16_to_lds(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               : : "v"(g), "s"(lds_base) : "memory", "m0");
-}
-// The same load addressed as a wave-uniform base (kept in SGPRs) plus a
+// wave writes the 16 bytes at sbase + voff (its own offset) to LDS byte
+// address lds_base + 16 * i (lds_base must be wave-uniform).  Written as
+// inline asm so that the compiler does not treat it as a pending write to all
+// of LDS: it would otherwise make every later LDS read it cannot disambiguate
+// (the transposing reads, for instance) wait for the load.  The instruction
+// has no result register; completion is tracked by vmcnt, so the caller
+// waits with s_waitcnt vmcnt before a barrier that publishes the data.
+//
+// The load is addressed as a wave-uniform base (kept in SGPRs) plus a
 // per-lane 32-bit byte offset: no 64-bit address arithmetic per lane.
 // `sbase` must be the same in every lane; it is read from the first active
 // lane so that the compiler keeps it in scalar registers.
+//
+// The LDS address goes through M0, which the statement writes itself (M0 is
+// declared clobbered).  The CDNA3/CDNA4 ISA requires one wait state between an
+// SALU write of M0 and an LDS-DMA load that reads it ("manually inserted wait
+// states": SALU writes M0, then a global or buffer load with LDS = 1), and
+// the compiler cannot insert it inside an asm statement, so the statement
+// carries its own s_nop 0.  Without it the load may still see the M0 value
+// from before the write, i.e. land on the LDS rows of an earlier load.
 __device__ __forceinline__ void dma16_to_lds_sv(const void* sbase, uint32_t voff,
                                                 uint32_t lds_base) {
   // (readfirstlane returns a signed int: each half goes through uint32_t so
@@ -129,12 +134,7 @@ __device__ __forceinline__ void dma16_to_lds_sv(const void* sbase, uint32_t voff
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
   const uint64_t u = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
-  // M0 (the LDS address) is written inside the statement and declared
-  // clobbered.  Passing it as an input operand ("{m0}") instead let the
-  // compiler drop the wait state it keeps between consecutive statements of
-  // this kind (it cannot see that the load reads M0), and that form faulted
-  // the GPU; it is not used.
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                : : "v"(voff), "s"(u), "s"(lds_base) : "memory", "m0");
 }
 // LDS byte address of a pointer into a __shared__ array.

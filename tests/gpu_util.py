@@ -10,12 +10,13 @@ import qwen3_gqa_attention_amd as q3
 from workloads import EPS, ROPE_THETA
 
 # Pass bar: fp32 max abs error <= 1e-4; bf16 max abs <= 2e-2 and rel L2 <= 1e-2.
-# The bf16 absolute bar is stated for outputs of magnitude up to 4; above that
-# the bf16 output format alone exceeds it (half an ulp is 2^-5 = 0.031 for
-# |y| in [8, 16): the exact result of the 64-head / 4-KV-head workload,
-# max|Y| = 8.95, rounded once to bf16 is already 0.0216 away).  So the
-# absolute bar scales with the reference's magnitude beyond 4:
-#   max abs <= 2e-2 * max(1, max|ref| / 4).
+# The bf16 absolute bar holds element by element for outputs of magnitude up
+# to 4.  Above that the bf16 output format alone exceeds it (half an ulp is
+# 2^-5 = 0.031 for |y| in [8, 16): the exact result of the 64-head / 4-KV-head
+# workload, max|Y| = 8.95, rounded once to bf16 is already 0.0216 away), so
+# the bar of element i scales with that element's own reference value:
+#   |got_i - ref_i| <= 2e-2 * max(1, |ref_i| / 4).
+# Elements with |ref_i| <= 4 therefore meet the stated 2e-2 exactly.
 TOL = {"f32": dict(max_abs=1e-4, rel_l2=None, scale_above=None),
        "bf16": dict(max_abs=2e-2, rel_l2=1e-2, scale_above=4.0)}
 
@@ -54,21 +55,34 @@ def errors(got, ref):
     return max_abs, rel
 
 
-def max_abs_bar(ref, dtype) -> float:
+def element_bars(ref, dtype) -> np.ndarray:
+    """The absolute bar of every element (see TOL)."""
     tol = TOL[dtype]
+    ref = np.abs(np.asarray(ref, np.float64))
     if tol["scale_above"] is None:
-        return tol["max_abs"]
-    peak = float(np.max(np.abs(ref))) if np.size(ref) else 0.0
-    return tol["max_abs"] * max(1.0, peak / tol["scale_above"])
+        return np.full(ref.shape, tol["max_abs"])
+    return tol["max_abs"] * np.maximum(1.0, ref / tol["scale_above"])
 
 
 def assert_close(got, ref, dtype, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
     max_abs, rel = errors(got, ref)
     tol = TOL[dtype]
-    bar = max_abs_bar(ref, dtype)
-    print(f"  {what}: max_abs={max_abs:.3e} (bar {bar:.3e}) rel_l2={rel:.3e}", flush=True)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} != {ref.shape}"
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    assert max_abs <= bar, f"{what}: max abs {max_abs:.3e} > {bar:.3e}"
+    diff = np.abs(got - ref)
+    bars = element_bars(ref, dtype)
+    worst = float(np.max(diff / bars)) if diff.size else 0.0
+    small = np.abs(ref) <= (tol["scale_above"] or np.inf)
+    max_small = float(np.max(diff[small])) if np.any(small) else 0.0
+    n_over = int(np.sum(diff > tol["max_abs"]))
+    print(f"  {what}: max_abs={max_abs:.3e} (|ref|<=4: {max_small:.3e}, nominal bar "
+          f"{tol['max_abs']:.0e}; {n_over} of {diff.size} elements above it) "
+          f"worst err/bar={worst:.3f} rel_l2={rel:.3e}" if tol["scale_above"] else
+          f"  {what}: max_abs={max_abs:.3e} (bar {tol['max_abs']:.0e}) rel_l2={rel:.3e}", flush=True)
+    assert worst <= 1.0, (f"{what}: element error {worst:.3f}x its bar "
+                          f"(max abs {max_abs:.3e}; |ref|<=4 max abs {max_small:.3e})")
     if tol["rel_l2"] is not None:
         assert rel <= tol["rel_l2"], f"{what}: rel L2 {rel:.3e} > {tol['rel_l2']}"
 

@@ -155,3 +155,37 @@ def test_status_strings(built_lib):
     for code in range(6):
         assert q3.qwen3_attn_status_string(code)
     assert q3.qwen3_attn_status_string(99) == "unknown status"
+
+
+def test_binding_keeps_one_workspace_per_stream(monkeypatch):
+    # The wrapper's own workspace (used when the caller passes none) is cached
+    # per stream: two streams never share scratch memory, a stream reuses its
+    # buffer while it is large enough, and a caller's workspace is passed
+    # through untouched.  A stand-in for torch supplies the current stream.
+    import types
+
+    import torch
+
+    current = {"stream": 11}
+    fake = types.SimpleNamespace(
+        uint8=torch.uint8,
+        cuda=types.SimpleNamespace(current_stream=lambda: types.SimpleNamespace(
+            cuda_stream=current["stream"])),
+        empty=lambda n, dtype=None, device=None: torch.empty(n, dtype=dtype))
+    monkeypatch.setattr(q3, "_torch", lambda: fake)
+    obj = q3.Qwen3Attention.__new__(q3.Qwen3Attention)
+    obj.handle = 0
+    obj._ws = {}
+    a = obj._workspace(100, None)
+    assert obj._workspace(80, None) is a           # same stream, fits: reused
+    current["stream"] = 22
+    b = obj._workspace(100, None)
+    assert b is not a and b.data_ptr() != a.data_ptr()   # another stream: its own buffer
+    current["stream"] = 11
+    assert obj._workspace(100, None) is a
+    c = obj._workspace(400, None)                  # grows on its own stream only
+    assert c is not a and c.numel() >= 400 and obj._workspace(10, None) is c
+    current["stream"] = 22
+    assert obj._workspace(10, None) is b
+    mine = torch.empty(5, dtype=torch.uint8)
+    assert obj._workspace(10 ** 6, mine) is mine   # the caller's workspace is used as given

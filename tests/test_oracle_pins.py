@@ -399,6 +399,54 @@ def test_layer_decode_equals_last_layer_prefill_row():
     np.testing.assert_allclose(dec["Y"], full["Y"][:, 8], rtol=1e-12, atol=1e-13)
 
 
+def _torch_input_norm(x, g_in, eps=1e-6):
+    # torch's own RMSNorm with a weight, in float64 (the oracle's rms_norm is not used)
+    t = torch.from_numpy(np.asarray(x, np.float64))
+    return F.rms_norm(t, (t.shape[-1],), weight=torch.from_numpy(np.asarray(g_in, np.float64)),
+                      eps=eps).numpy()
+
+
+def test_layer_input_gain_closed_form_with_zero_query_weight():
+    # Wq = 0: q~ = 0, every visible key gets the same weight, so the block's
+    # attention output is the prefix mean of V = (RMSNorm(x) * g_in) Wv^T and
+    # the layer returns y_t = x_t + Wo . concat_h mean_{j<=t} V_{j, h // n_rep}
+    # ("Assembling a large model from scratch", section "The complete code":
+    # input_layernorm with its weight, attention, residual add).  V depends on
+    # the input gain g_in element by element, so a dropped, squared or
+    # misplaced gain fails here.
+    p = rand_block(34, B=2, T=9, d=48, n_q=6, n_kv=3)
+    g_in = 1 + 0.3 * np.random.default_rng(4).standard_normal(48)
+    a = residual_args(p)
+    a["wq"] = np.zeros_like(a["wq"])
+    x = a.pop("x")
+    out = oracle.prefill_residual(x, g_in, **a, n_q=6, n_kv=3, dh=16)
+    v = (_torch_input_norm(x, g_in) @ p["wv"].T).reshape(2, 9, 3, 16)
+    pref = np.cumsum(v, axis=1) / np.arange(1, 10)[None, :, None, None]
+    cat = np.concatenate([pref[:, :, h // 2] for h in range(6)], axis=-1)
+    np.testing.assert_allclose(out["Y"], x + cat @ p["wo"].T, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_decode_input_gain_closed_form_with_zero_query_weight():
+    # The same closed form for one decode step: the new token (position L)
+    # weighs the L cached values and its own value V = (RMSNorm(x) * g_in) Wv^T
+    # equally, y = x + Wo . concat_h mean(V_cache[0..L-1], V_new).
+    rng = np.random.default_rng(5)
+    p = rand_block(35, B=3, T=1, d=48, n_q=4, n_kv=2)
+    g_in = 1 + 0.3 * rng.standard_normal(48)
+    L = np.array([0, 3, 6])
+    kc = rng.standard_normal((3, 2, 8, 16))
+    vc = rng.standard_normal((3, 2, 8, 16))
+    x = p["x"][:, 0]
+    dec = oracle.decode_residual(x, g_in, np.zeros_like(p["wq"]), p["wk"], p["wv"], p["wo"],
+                                 p["gq"], p["gk"], L, kc, vc, n_q=4, n_kv=2, dh=16)
+    vnew = (_torch_input_norm(x, g_in) @ p["wv"].T).reshape(3, 2, 16)
+    for s in range(3):
+        allv = np.concatenate([vc[s][:, :L[s]], vnew[s][:, None]], axis=1)   # [n_kv, L+1, dh]
+        mean = allv.mean(axis=1)
+        cat = np.concatenate([mean[h // 2] for h in range(4)])
+        np.testing.assert_allclose(dec["Y"][s], x[s] + p["wo"] @ cat, rtol=1e-12, atol=1e-12)
+
+
 # --- sliding window ------------------------------------------------------
 # A layer with sliding window W keeps the W most recent keys, the query's own
 # included ("Qwen3 Architecture Layer-by-Layer", sections "Layer 1 -
