@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close, block_from_inputs, dev, from_paged, host, say, to_paged
+from gpu_util import (assert_close, block_from_inputs, dev, from_paged, host, say,
+                      storage_floor_rows, to_paged)
 from workloads import (EPS, ROPE_THETA, WORKLOADS, bf16_bits_to_f32, decode_cache_host,
                        prefill_inputs, round_to_bf16_bits)
 
@@ -110,7 +111,15 @@ def test_varlen_prefill_parity(idx, lens, past):
     got = run_varlen_gpu(w, inp, lens, past, cu, kc, vc)
     Y, rk, rv = oracle_varlen(w, inp, lens, past, cu, kc, vc)
     check_caches(w, got, kc, lens, past, rk, rv)
-    assert_close(got["Y"], Y, w.dtype, "packed output Y")
+    floor = None
+    if w.dtype == "bf16":
+        floor = np.concatenate([
+            storage_floor_rows(inp["X"][cu[b]:cu[b + 1]], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"],
+                               inp["gq"], inp["gk"], inp["positions"][cu[b]:cu[b + 1]],
+                               list(range(n)), n_q=w.n_q, n_kv=w.n_kv,
+                               past_k=kc[b][:, :past[b]], past_v=vc[b][:, :past[b]])
+            for b, n in enumerate(lens) if n > 0])
+    assert_close(got["Y"], Y, w.dtype, "packed output Y", floor=floor)
 
 
 def test_varlen_without_past_equals_empty_caches():
