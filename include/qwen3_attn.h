@@ -296,6 +296,29 @@ qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,
                                             void* workspace, size_t workspace_bytes,
                                             void* stream);
 
+/* Scratch bytes available to qwen3_attn_forward_decode_noalloc (64 MiB). */
+#define QWEN3_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory at all -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation:
+ * qwen3_attn_forward_decode with the same arguments, validation, kernels and
+ * results, minus the workspace.  Its scratch memory is a static device array
+ * of QWEN3_ATTN_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU,
+ * held until the process ends; the call allocates and frees nothing.
+ *   - A call whose qwen3_attn_workspace_size(desc, 1, N, 1, cache_cap) exceeds
+ *     QWEN3_ATTN_NOALLOC_SCRATCH_BYTES returns EWORKSPACE and launches
+ *     nothing (the 0.6B shape fits 64 sequences with caches of 32832 slots).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on a
+ *     GPU (several streams or host threads) race and give wrong results.
+ *     Serialise them, or use qwen3_attn_forward_decode with a workspace each.
+ *   - The first call on each device looks the array's device address up
+ *     (EHIP if that fails). */
+qwen3_attn_status qwen3_attn_forward_decode_noalloc(qwen3_attn_t* h, const void* hidden,
+                                                    const int32_t* positions,
+                                                    void* k_cache, void* v_cache,
+                                                    int64_t cache_cap, void* out, int32_t N,
+                                                    void* stream);
+
 /* Free the handle's device memory (synchronises the device first so no
  * enqueued work still reads it).  NULL is a no-op. */
 void qwen3_attn_destroy(qwen3_attn_t* h);

@@ -23,7 +23,8 @@ EXPORTED = ("qwen3_attn_create", "qwen3_attn_create_with_input_norm", "qwen3_att
             "qwen3_attn_forward_prefill",
             "qwen3_attn_forward_prefill_chunk", "qwen3_attn_forward_prefill_paged",
             "qwen3_attn_forward_prefill_varlen", "qwen3_attn_workspace_size_varlen",
-            "qwen3_attn_forward_decode", "qwen3_attn_forward_decode_paged", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
+            "qwen3_attn_forward_decode", "qwen3_attn_forward_decode_paged",
+            "qwen3_attn_forward_decode_noalloc", "qwen3_attn_destroy", "qwen3_attn_enable_stage_timing",
             "qwen3_attn_stage_times", "qwen3_attn_status_string")
 STAGES = ("qkv_norm_rope_gemm", "attention", "o_proj_gemm")
 
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.qwen3_attn_forward_decode_paged.restype = ctypes.c_int
         L.qwen3_attn_forward_decode.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, vp]
         L.qwen3_attn_forward_decode.restype = ctypes.c_int
+        L.qwen3_attn_forward_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp]
+        L.qwen3_attn_forward_decode_noalloc.restype = ctypes.c_int
         L.qwen3_attn_destroy.argtypes = [vp]
         L.qwen3_attn_destroy.restype = None
         L.qwen3_attn_enable_stage_timing.argtypes = [vp, i32]
@@ -173,6 +176,15 @@ def qwen3_attn_forward_decode(handle, hidden, positions, k_cache, v_cache, cache
                               workspace, workspace_bytes, stream) -> int:
     return lib().qwen3_attn_forward_decode(handle, hidden, positions, k_cache, v_cache, cache_cap,
                                            out, N, workspace, workspace_bytes, stream)
+
+
+def qwen3_attn_forward_decode_noalloc(handle, hidden, positions, k_cache, v_cache, cache_cap, out,
+                                      N, stream) -> int:
+    return lib().qwen3_attn_forward_decode_noalloc(handle, hidden, positions, k_cache, v_cache,
+                                                   cache_cap, out, N, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # QWEN3_ATTN_NOALLOC_SCRATCH_BYTES
 
 
 def qwen3_attn_destroy(handle) -> None:

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqwen3attn.so")
-SOURCES = ["gemm.hip", "flash_prefill.hip", "decode.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "flash_prefill.hip", "decode.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 
