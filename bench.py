@@ -141,17 +141,38 @@ def prefill_flops(B, T, d, n_q, n_kv, dh=128):
     }
 
 
+MIN_TIMED_S = 0.2      # duration-timed entries run at least this long ...
+MIN_TIMED_STEPS = 50   # ... and at least this many steps
+
+
+def steps_for_duration(step_s):
+    """Steps for a timed region of at least MIN_TIMED_S and MIN_TIMED_STEPS steps."""
+    import math
+    return max(MIN_TIMED_STEPS, int(math.ceil(MIN_TIMED_S / max(step_s, 1e-9))))
+
+
+def estimate_step_s(fn, n=5):
+    """Mean time of n back-to-back calls (after the caller's warm-up)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / n
+
+
 def bench_prefill(args, layer=False, idx=2, steps=None):
     """The prefill of workload idx (default: the 0.6B shape, B=2, T=2048); with
     layer=True the block carries the fused input RMSNorm and residual add (the
-    attention half of a decoder layer)."""
+    attention half of a decoder layer).  steps=None: args.steps (the headline);
+    steps="duration": enough steps for MIN_TIMED_S and MIN_TIMED_STEPS."""
     import numpy as np
     import torch
 
     import qwen3_gqa_attention_amd as q3
     from workloads import EPS, ROPE_THETA, WORKLOADS, prefill_inputs
 
-    steps = steps or args.steps
     w = WORKLOADS[idx]
     B, T = w.B, w.T
     inp = prefill_inputs(w)
@@ -173,6 +194,10 @@ def bench_prefill(args, layer=False, idx=2, steps=None):
     for _ in range(args.warmup):
         blk.prefill(x, pos, kc, vc, out=out, workspace=ws)
     torch.cuda.synchronize()
+    if steps == "duration":
+        steps = steps_for_duration(estimate_step_s(
+            lambda: blk.prefill(x, pos, kc, vc, out=out, workspace=ws)))
+    steps = steps or args.steps
 
     # timed region 1: K plain steps -> the reported throughput
     t0 = time.perf_counter()
@@ -207,7 +232,7 @@ def bench_prefill(args, layer=False, idx=2, steps=None):
     total_flops = sum(flops.values())
     blk.close()
     return dict(B=B, T=T, w=w, step_s=step_s, step_events_s=step_events_s, kernels=kernels,
-                dominant=dom, flops=flops, total_flops=total_flops, ncalls=ncalls)
+                dominant=dom, flops=flops, total_flops=total_flops, ncalls=ncalls, steps=steps)
 
 
 def chunk_flops(B, T, P, d, n_q, n_kv, dh=128):
@@ -248,19 +273,21 @@ def bench_chunk(args, P=1536, T=512):
     for _ in range(args.warmup):
         blk.prefill_chunk(x, pos, past, kc, vc, out=out, workspace=ws)
     torch.cuda.synchronize()
+    steps = steps_for_duration(estimate_step_s(
+        lambda: blk.prefill_chunk(x, pos, past, kc, vc, out=out, workspace=ws)))
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         blk.prefill_chunk(x, pos, past, kc, vc, out=out, workspace=ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    blk.enable_stage_timing(args.steps)
-    for _ in range(args.steps):
+    blk.enable_stage_timing(steps)
+    for _ in range(steps):
         blk.prefill_chunk(x, pos, past, kc, vc, out=out, workspace=ws)
     torch.cuda.synchronize()
     stage_ms, ncalls = blk.stage_times()
     blk.enable_stage_timing(0)
     blk.close()
-    step_s = (t1 - t0) / args.steps
+    step_s = (t1 - t0) / steps
     flops = chunk_flops(B, T, P, w.d, w.n_q, w.n_kv)
     kernels = {}
     for name, tot in zip(q3.STAGES, stage_ms):
@@ -269,7 +296,7 @@ def bench_chunk(args, P=1536, T=512):
                          "frac_mfma_peak": flops[name] / avg / PEAK_BF16_FLOPS}
     total = sum(flops.values())
     return {"workload": f"{w.name}-chunk-T{T}-past{P}", "B": B, "T": T, "past": P,
-            "ms_per_step": step_s * 1e3, "tokens_per_s": B * T / step_s,
+            "steps": steps, "ms_per_step": step_s * 1e3, "tokens_per_s": B * T / step_s,
             "tflops": total / step_s / 1e12, "frac_mfma_peak": total / step_s / PEAK_BF16_FLOPS,
             "kernels": kernels}
 
@@ -435,30 +462,69 @@ def bench_prefill_cold(args, calls=50, flush_mb=512):
     return res
 
 
-def cpu_baseline(seconds):
-    """The fp64 oracle's own code run in float32 on host cores, bounded sample."""
-    import numpy as np
+def cpu_info():
+    """The host CPU's model name and logical CPU count, and the BLAS threads numpy uses."""
     from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return model, os.cpu_count(), int(threads)
+
+
+def cpu_baseline():
+    """The oracle (its own code, run in float32) on the host's cores: the
+    headline prefill (median of 3), the 4B prefill (one run), the wide-GQA
+    shape over its first 2048 tokens (one run), and one decode step of 8 of the
+    64 decode sequences at their own cache lengths.  About 20-40 s of CPU."""
+    import statistics
+
+    import numpy as np
 
     import oracle
-    from workloads import EPS, ROPE_THETA, WORKLOADS, prefill_inputs
+    from workloads import (EPS, ROPE_THETA, WORKLOADS, decode_cache_host, decode_inputs,
+                           prefill_inputs)
 
-    w = WORKLOADS[2]
-    T = w.T
-    inp = prefill_inputs(w, B=1, T=T)
-    args = [inp[k] for k in ("X", "Wq", "Wk", "Wv", "Wo", "gq", "gk", "positions")]
-    reps = 0
+    def prefill_time(idx, T=None):
+        w = WORKLOADS[idx]
+        inp = prefill_inputs(w, T=T)
+        a = [inp[k] for k in ("X", "Wq", "Wk", "Wv", "Wo", "gq", "gk", "positions")]
+        t0 = time.perf_counter()
+        oracle.prefill(*a, n_q=w.n_q, n_kv=w.n_kv, eps=EPS, theta=ROPE_THETA, dtype=np.float32)
+        return time.perf_counter() - t0, w, inp["X"].shape[0] * inp["X"].shape[1]
+
+    runs = [prefill_time(2) for _ in range(3)]
+    head_s = statistics.median(r[0] for r in runs)
+    tokens = runs[0][2]
+    other = {}
+    for idx, T, note in ((3, None, "one run, full size"), (4, 2048, "one run, first 2048 tokens")):
+        t, w, n = prefill_time(idx, T)
+        other[w.name] = {"sample": note, "tokens": n, "seconds": t, "tokens_per_s": n / t}
+    # decode: 8 of the 64 sequences (the first 8 of the seeded draw), their caches on the host
+    w = WORKLOADS[5]
+    full = decode_inputs(w)
+    lens = full["lengths"][:8].astype(np.int32)
+    inp = decode_inputs(w, N=8)
+    kc, vc = decode_cache_host(w, lens, int(lens.max()) + 1)
     t0 = time.perf_counter()
-    while True:
-        oracle.prefill(*args, n_q=w.n_q, n_kv=w.n_kv, eps=EPS, theta=ROPE_THETA, dtype=np.float32)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": reps * T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} x oracle.prefill (float32) of one B=1,T={T} sequence of the "
-                      f"0.6B-shaped workload, {el:.1f} s; host has {os.cpu_count()} logical CPUs"}
+    oracle.decode(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], inp["gq"], inp["gk"], lens,
+                  kc, vc, n_q=w.n_q, n_kv=w.n_kv, eps=EPS, theta=ROPE_THETA, dtype=np.float32)
+    dt = time.perf_counter() - t0
+    nbytes = float(lens.astype(np.int64).sum()) * 2 * w.n_kv * 128 * 2   # bf16 cache rows read
+    other[w.name] = {"sample": "one step of 8 of the 64 sequences", "cache_tokens": int(lens.sum()),
+                     "seconds": dt, "tokens_per_s": 8 / dt, "GBps_bf16_cache_bytes": nbytes / dt / 1e9}
+    model, ncpu, threads = cpu_info()
+    return {"value": tokens / head_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"median of 3 oracle.prefill (float32) runs of the full B=2, T=2048 0.6B-shaped "
+                      f"batch ({', '.join(f'{r[0]:.2f}' for r in runs)} s); host: {model}, "
+                      f"{ncpu} logical CPUs, numpy BLAS on {threads} threads",
+            "cpu_model": model, "logical_cpus": ncpu, "other": other}
 
 
 def main():
@@ -467,12 +533,14 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="run only the prefill step and the full-attention decode (the two "
                          "roofline kernels), e.g. under a profiler")
+    ap.add_argument("--only", choices=["4b", "wide-gqa", "chunk"],
+                    help="time one secondary prefill workload alone and print its own JSON line "
+                         "(for profiling it by itself; not the headline line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy of known size (for PMC traffic calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -496,6 +564,18 @@ def main():
         build()
     torch.cuda.set_device(0)
 
+    if args.only:
+        if args.only == "chunk":
+            r = bench_chunk(args)
+        else:
+            pc = bench_prefill(args, idx=3 if args.only == "4b" else 4, steps="duration")
+            r = {"workload": pc["w"].name, "B": pc["B"], "T": pc["T"], "steps": pc["steps"],
+                 "ms_per_step": pc["step_s"] * 1e3,
+                 "tokens_per_s": pc["B"] * pc["T"] / pc["step_s"],
+                 "frac_mfma_peak": pc["total_flops"] / pc["step_s"] / PEAK_BF16_FLOPS,
+                 "kernels": pc["kernels"]}
+        print(json.dumps(r), flush=True)
+        return
     if args.copy_calibration:
         copy_calibration()
     traffic = load_traffic()
@@ -521,10 +601,10 @@ def main():
         log(f"bench: prefill per call: hot median {cold['hot']['median_ms']:.4f} ms, "
             f"cold median {cold['cold']['median_ms']:.4f} ms")
         for idx in (3, 4):
-            pc = bench_prefill(args, idx=idx, steps=max(args.steps // (4 if idx == 3 else 20), 5))
+            pc = bench_prefill(args, idx=idx, steps="duration")
             wc = pc["w"]
             other[wc.name] = {
-                "B": pc["B"], "T": pc["T"], "ms_per_step": pc["step_s"] * 1e3,
+                "B": pc["B"], "T": pc["T"], "steps": pc["steps"], "ms_per_step": pc["step_s"] * 1e3,
                 "tokens_per_s": pc["B"] * pc["T"] / pc["step_s"],
                 "tflops": pc["total_flops"] / pc["step_s"] / 1e12,
                 "frac_mfma_peak": pc["total_flops"] / pc["step_s"] / PEAK_BF16_FLOPS,
@@ -573,7 +653,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle, float32)")
-        cpu = cpu_baseline(args.cpu_seconds)
+        cpu = cpu_baseline()
 
     w = p["w"]
     dom = p["dominant"]

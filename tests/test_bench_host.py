@@ -86,3 +86,11 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_duration_timed_entries_run_long_enough():
+    # the 4B, wide-GQA and chunked prefills are timed over at least
+    # MIN_TIMED_STEPS steps and MIN_TIMED_S seconds, whatever --steps says
+    assert bench.steps_for_duration(2e-3) == max(bench.MIN_TIMED_STEPS, 100)
+    assert bench.steps_for_duration(6.4e-5) * 6.4e-5 >= bench.MIN_TIMED_S
+    assert bench.steps_for_duration(10.0) == bench.MIN_TIMED_STEPS
