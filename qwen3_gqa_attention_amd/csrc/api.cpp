@@ -7,6 +7,7 @@
 
 #include <climits>
 #include <cmath>
+#include <cstring>
 #include <new>
 
 #include "kernels.hpp"
@@ -22,6 +23,12 @@ struct qwen3_attn {
   float* rope_rev;   // [128]: omega_i / (2 pi) as hi [0..63] + lo [64..127] floats,
                      // omega_i = theta^(-2i/128)
   float rope_rev_host[128];
+  // Bound on |q~ . k~| (the attention scores in the log2 units of the exponent)
+  // for keys this handle's QK-Norm produced: q_norm / k_norm leave every head
+  // vector with norm <= sqrt(d_head) * max|gain| ("Qwen 3 From Scratch",
+  // section "The idea": RMS-normalised q and k, which bounds the logits), RoPE
+  // keeps the norm, and q~ carries log2(e) / sqrt(d_head).
+  float score_bound;
   int in_norm;       // 1: forward = hidden + block(RMSNorm(hidden) * input gain)
   // measurement aid: events before each kernel and after the last
   int timing_cap;
@@ -153,6 +160,13 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   q3::QkvEpilogue e{qbuf, k_cache, v_cache, positions, h->g_q, h->g_k, h->rope_rev,
                     d.n_q, d.n_kv, kv, T_len, 0, d.eps, past,
                     h->in_norm ? hidden : nullptr, q3::kScoreScaleLog2, cu_seqlens, B};
+  // Over empty caches every key of the call comes from this call's QK-Norm, so
+  // the handle's score bound holds and the attention can use it as a fixed
+  // softmax reference; keys already in a cache were written by someone else.
+  const float fixed_ref =
+      (past == nullptr && h->score_bound > 0.f && h->score_bound <= q3::kMaxFixedRef)
+          ? h->score_bound
+          : 0.f;
   mark(h, s, 0);
   hipError_t r = q3::launch_qkv_gemm<T>(reinterpret_cast<const T*>(hidden),
                                         reinterpret_cast<const T*>(h->w_qkv), M, nqkv, d.d_model,
@@ -162,7 +176,7 @@ qwen3_attn_status run_prefill(qwen3_attn_t* h, const void* hidden, const int32_t
   r = q3::launch_flash_prefill<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                   reinterpret_cast<const T*>(v_cache), abuf, B, T_len, cu_seqlens,
                                   n_tok, d.n_q, d.n_kv, kv, past, d.sliding_window,
-                                  reinterpret_cast<float*>(ws + L.part_off), s);
+                                  reinterpret_cast<float*>(ws + L.part_off), fixed_ref, s);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   mark(h, s, 2);
   r = q3::launch_proj_gemm<T>(abuf, reinterpret_cast<const T*>(h->w_o), reinterpret_cast<T*>(out),
@@ -276,6 +290,33 @@ qwen3_attn_status create_impl(const qwen3_attn_desc* desc, const qwen3_attn_weig
                                                    static_cast<const q3::bf16_t*>(input_norm), s);
   }
   if (r == hipSuccess) r = hipStreamSynchronize(s);  // the host copy of rope_rev must complete
+  // The gains' largest magnitudes give the score bound (see struct qwen3_attn):
+  // |q~ . k~| <= scale * (sqrt(128) max|g_q|) * (sqrt(128) max|g_k|), times a
+  // margin for the bf16 rounding of q~ and k~ (each norm grows by at most
+  // 2^-9) and fp32 rounding in the norm, RoPE and the dot product.
+  float gq_max = 0.f, gk_max = 0.f;
+  if (r == hipSuccess) {
+    unsigned char gbuf[2][128 * 4];
+    r = hipMemcpy(gbuf[0], h->g_q, 128 * es, hipMemcpyDeviceToHost);
+    if (r == hipSuccess) r = hipMemcpy(gbuf[1], h->g_k, 128 * es, hipMemcpyDeviceToHost);
+    for (int w = 0; w < 2 && r == hipSuccess; ++w) {
+      float mx = 0.f;
+      for (int i = 0; i < 128; ++i) {
+        float v;
+        if (es == 4) {
+          std::memcpy(&v, gbuf[w] + 4 * i, 4);
+        } else {
+          uint16_t b;
+          std::memcpy(&b, gbuf[w] + 2 * i, 2);
+          const uint32_t u = static_cast<uint32_t>(b) << 16;
+          std::memcpy(&v, &u, 4);
+        }
+        mx = std::isfinite(v) ? std::fmax(mx, std::fabs(v)) : INFINITY;
+      }
+      (w == 0 ? gq_max : gk_max) = mx;
+    }
+  }
+  h->score_bound = q3::kScoreScaleLog2 * 128.f * gq_max * gk_max * (1.f + 1.f / 64.f);
   if (r != hipSuccess) {
     (void)hipFree(h->mem);
     delete h;

@@ -53,7 +53,18 @@ __device__ __forceinline__ v4bf16_t ds_read_tr16(const bf16_t* p) {
       (lds_v4bf16_t*)(__attribute__((address_space(3))) bf16_t*)(p));
 }
 
-template <typename T, int KSPLIT>
+// FIXED: the softmax reference is the constant fixed_ref instead of a running
+// max.  softmax(s) = 2^(s - m) / sum 2^(s - m) for any finite m, so any
+// reference gives the same O / l; a running max is only needed to keep
+// 2^(s - m) inside the floating-point range.  When every score is known to
+// lie in [-fixed_ref, fixed_ref] with fixed_ref <= kMaxFixedRef, m = fixed_ref
+// keeps every probability in [2^-2 kMaxFixedRef, 1] -- normal numbers in fp32
+// and in bf16 (same exponent range), so P keeps its full relative precision --
+// and the per-tile max, its cross-lane exchange, the rescale test and the
+// rescale itself all drop out of the key loop.  The host passes such a bound
+// when every key of the call comes from this call's QK-Norm (see
+// qwen3_attn_create).
+template <typename T, int KSPLIT, bool FIXED>
 __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T* __restrict__ Q,
                                                             const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc,
@@ -63,7 +74,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             int n_q, int n_kv, KvAddr kv,
                                                             const int32_t* __restrict__ past,
                                                             int window, int nsplit,
-                                                            float* __restrict__ part) {
+                                                            float* __restrict__ part,
+                                                            float fixed_ref) {
   using MF = Mfma32<T>;
   constexpr int BN = FlashTile<T>::BN;
   constexpr int NKB = BN / 32;                 // 32-key blocks per tile
@@ -243,8 +255,12 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // below their running max (see the rescale below), -inf until this lane has
   // seen a key.  The score accumulators start at -m_run (0 while m_run is
   // -inf), so they come out of the MFMAs already relative to it.
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = FIXED ? fixed_ref : -INFINITY, l_run = 0.f;
   f32x16_v mbias = f32x16_v{};
+  if constexpr (FIXED) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mbias[i] = -fixed_ref;
+  }
 
   // One key tile from stage P (0 or 1, a compile-time constant) of this
   // wave's key half.
@@ -348,6 +364,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
           for (int i = 0; i < 16; ++i)
             if (kb * 32 + 8 * (i >> 2) + (i & 3) < lo) s[kb][i] = -INFINITY;
       }
+      if constexpr (!FIXED) {
       // Tile max relative to the running max; the two half-waves hold the
       // two halves of each query's keys.
       float mloc = -INFINITY;
@@ -387,6 +404,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
         const float nb = m_run == -INFINITY ? 0.f : -m_run;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mbias[i] = nb;
+      }
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -501,7 +519,14 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   }
   lds_barrier();
   if (kh == 1) return;
-  {
+  if constexpr (FIXED) {
+    // both halves are relative to the same reference: plain sums
+    l_run += comb[65 * 64 + lane];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] += comb[(db * 16 + i) * 64 + lane];
+  } else {
     const float m1 = comb[64 * 64 + lane], l1 = comb[65 * 64 + lane];
     const float M = fmaxf(m_run, m1);
     const float a0 = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
@@ -602,24 +627,39 @@ size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv, int n_tok) {
   return sp > 1 ? (size_t)sp * n_tok * n_q * (kHeadDim + 2) : 0;
 }
 
+template <typename T, bool FIXED>
+static void launch_flash_kernel(int wgs, const T* Q, const T* Kc, const T* Vc, T* Out, int B,
+                                int T_len, const int32_t* cu_seqlens, int n_tok, int n_q, int n_kv,
+                                const KvAddr& kv, const int32_t* past, int window, int nsplit,
+                                float* part, float fixed_ref, hipStream_t s) {
+  // Few workgroups: split each query tile's key range over two wave groups
+  // so both waves of a SIMD serve the same tile.  Many: 4-wave workgroups,
+  // two resident per CU.
+  if (wgs < 4 * 256)
+    hipLaunchKernelGGL((flash_prefill_kernel<T, 2, FIXED>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc,
+                       Out, B, T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part,
+                       fixed_ref);
+  else
+    hipLaunchKernelGGL((flash_prefill_kernel<T, 1, FIXED>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc,
+                       Out, B, T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part,
+                       fixed_ref);
+}
+
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
                                 const int32_t* cu_seqlens, int n_tok, int n_q, int n_kv,
                                 const KvAddr& kv, const int32_t* past, int window, float* part,
-                                hipStream_t s) {
-  if (window < 0) return hipErrorInvalidValue;
+                                float fixed_ref, hipStream_t s) {
+  if (window < 0 || !(fixed_ref >= 0.f) || fixed_ref > kMaxFixedRef) return hipErrorInvalidValue;
   const int nsplit = flash_splits(B, T_len, n_q, n_kv);
   if (nsplit > 1 && !part) return hipErrorInvalidValue;
-  // Few workgroups: split each query tile's key range over two wave groups
-  // so both waves of a SIMD serve the same tile.  Many: 4-wave workgroups,
-  // two resident per CU.
   const int wgs = flash_query_wgs(B, T_len, n_q, n_kv) * nsplit;
-  if (wgs < 4 * 256)
-    hipLaunchKernelGGL((flash_prefill_kernel<T, 2>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part);
+  if (fixed_ref > 0.f)
+    launch_flash_kernel<T, true>(wgs, Q, Kc, Vc, Out, B, T_len, cu_seqlens, n_tok, n_q, n_kv, kv,
+                                 past, window, nsplit, part, fixed_ref, s);
   else
-    hipLaunchKernelGGL((flash_prefill_kernel<T, 1>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc, Out, B,
-                       T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part);
+    launch_flash_kernel<T, false>(wgs, Q, Kc, Vc, Out, B, T_len, cu_seqlens, n_tok, n_q, n_kv, kv,
+                                  past, window, nsplit, part, 0.f, s);
   if (nsplit > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -632,11 +672,11 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
 
 template hipError_t launch_flash_prefill<float>(const float*, const float*, const float*, float*,
                                                 int, int, const int32_t*, int, int, int,
-                                                const KvAddr&, const int32_t*, int, float*,
+                                                const KvAddr&, const int32_t*, int, float*, float,
                                                 hipStream_t);
 template hipError_t launch_flash_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
                                                  bf16_t*, int, int, const int32_t*, int, int, int,
-                                                 const KvAddr&, const int32_t*, int, float*,
+                                                 const KvAddr&, const int32_t*, int, float*, float,
                                                  hipStream_t);
 
 }  // namespace q3

@@ -117,11 +117,16 @@ int small_m_partial_floats(int M, int N, int K, int elem_size);
 // `part`: fp32 scratch of flash_partial_floats(...) floats (may be null when
 // that is 0): with few query tiles the key ranges are split over more
 // workgroups and merged by a second kernel.
+// fixed_ref in (0, kMaxFixedRef]: every score of the call (q~ . k~ in the
+// log2 units of the exponent) is known to lie in [-fixed_ref, fixed_ref];
+// the softmax then uses that constant reference instead of a running max.
+// 0: running max (no bound known, e.g. keys the call did not write).
+constexpr float kMaxFixedRef = 50.f;
 template <typename T>
 hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, int B, int T_len,
                                 const int32_t* cu_seqlens, int n_tok, int n_q, int n_kv,
                                 const KvAddr& kv, const int32_t* past, int window, float* part,
-                                hipStream_t s);
+                                float fixed_ref, hipStream_t s);
 int flash_splits(int B, int T_len, int n_q, int n_kv);
 size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv, int n_tok);
 

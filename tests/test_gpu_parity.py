@@ -85,6 +85,30 @@ def test_prefill_parity(idx, B, T):
     assert_close(got["Y"], ref["Y"], w.dtype, "block output Y", floor=floor)
 
 
+@pytest.mark.parametrize("dtype,gain", [("bf16", 1.71875), ("f32", 1.71875), ("bf16", 1.75),
+                                        ("f32", 1.75)])
+def test_prefill_scores_at_the_fixed_reference_limit(dtype, gain):
+    # Over empty caches the attention takes the handle's score bound
+    # 16.32 * max|g_q| * max|g_k| * (1 + 1/64) (log2 units) as a fixed softmax
+    # reference while it is <= 50.  Constant gains of 1.71875 put it at 48.97,
+    # just inside; 1.75 gives 50.77 and the running-max path.  With Wq = Wk
+    # (16 query heads, 16 KV heads) each token's own score equals the
+    # unmargined bound, 48.2, the largest a score can be, while others reach
+    # down to about -48: probabilities from about 2^-97 to 1.
+    w = dataclasses.replace(WORKLOADS[2], dtype=dtype, n_q=16, n_kv=16)
+    B, T = 1, 300
+    say(f"prefill at the fixed-reference limit: dtype={dtype} gains={gain}")
+    inp = prefill_inputs(w, B=B, T=T)
+    inp["Wk"] = inp["Wq"].copy()
+    inp["gq"] = np.full(128, gain, np.float32)
+    inp["gk"] = np.full(128, gain, np.float32)
+    got = run_prefill_gpu(w, inp, B, T)
+    ref = oracle_prefill(inp, w)
+    assert_close(got["Kc"][:, :, :T], ref["Kc"], w.dtype, "k cache")
+    floor = storage_floor_prefill(inp, w, B, T) if w.dtype == "bf16" else None
+    assert_close(got["Y"], ref["Y"], w.dtype, "block output Y", floor=floor)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_full_size_0p6b(dtype):
     # The benchmark's workload, compared in full; in fp32 too, which takes the
