@@ -75,7 +75,7 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
                                                             const int32_t* __restrict__ past,
                                                             int window, int nsplit,
                                                             float* __restrict__ part,
-                                                            float fixed_ref) {
+                                                            float fixed_ref, int items) {
   using MF = Mfma32<T>;
   constexpr int BN = FlashTile<T>::BN;
   constexpr int NKB = BN / 32;                 // 32-key blocks per tile
@@ -112,17 +112,25 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int bg = blockIdx.x % groups;
   const int rest = blockIdx.x / groups;
   const int split = rest % nsplit;
-  // Query tiles are issued heaviest (longest key range) first, so lighter
-  // ones fill CUs as they free up.
-  const int qt = tiles_per_group - 1 - rest / nsplit;
   const int b = bg / n_kv, g = bg % n_kv;
+  // Query tiles are issued heaviest (longest key range) first, so lighter
+  // ones fill CUs as they free up.  A paired workgroup (items == 2) runs two
+  // work items of the same (sequence, KV head): the heavy query tile
+  // tiles_per_group - 1 - j, then the light tile j, so that every workgroup
+  // carries the same number of key tiles, and the second item's Q fragments
+  // and first K/V tiles are loaded while the first item is merged and
+  // stored.
+  auto qt_of = [&](int item) {
+    const int j = rest / nsplit;
+    return item == 0 ? tiles_per_group - 1 - j : j;
+  };
   // Token rows of sequence b: q0 .. q0 + Tb - 1 (a variable-length batch
   // gives them in cu_seqlens; else every sequence has T_len).  Query tiles
   // past a shorter sequence's end have no work.
   const int q0 = cu_seqlens ? cu_seqlens[b] : b * T_len;
   const int Tb = cu_seqlens ? cu_seqlens[b + 1] - q0 : T_len;
   const int rows_total = Tb * n_rep;
-  if (qt * 128 >= rows_total) return;  // whole workgroup, before any barrier
+  if (qt_of(0) * 128 >= rows_total) return;  // whole workgroup, before any barrier
   // Chunked prefill: the sequence already holds P cached tokens, chunk token
   // t is key P + t and sees keys 0 .. P + t (P = 0 for a first prefill).
   const int P = past ? past[b] : 0;
@@ -136,40 +144,48 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   const int th = tid & 255;                    // thread index inside the key half
   const int c32 = lane & 31, hk = lane >> 5;
 
-  const int R0 = qt * 128;
-  const int Rw = R0 + qblk * 32;
-  const int Rl = Rw + c32;
-  const bool row_ok = Rl < rows_total;
-  const int qtok = row_ok ? Rl / n_rep : Tb - 1;      // token inside the chunk
-  const int tok = P + qtok;                            // its key position
-  const int head = g * n_rep + (row_ok ? Rl % n_rep : 0);
-  const bool wave_active = Rw < rows_total;
-  const int w_tok_lo = P + min(Rw, rows_total - 1) / n_rep;
-  const int w_tok_hi = P + min(Rw + 31, rows_total - 1) / n_rep;
-  // Sliding window W (0: none): key position j is visible to the token at
-  // key position i iff i - W < j <= i.  key_lo is this lane's first visible
-  // key; keys below w_mask_lo are masked for at least one row of the wave.
-  const int key_lo = window > 0 ? tok - window + 1 : 0;
-  const int w_key_lo = window > 0 ? w_tok_lo - window + 1 : 0;
-  const int w_mask_lo = window > 0 ? w_tok_hi - window + 1 : 0;
-  // Key tiles of the workgroup: from the first key its first row sees to the
-  // last key its last row sees.
-  const int kmax = P + min(R0 + 127, rows_total - 1) / n_rep;
-  const int kmin = window > 0 ? max(0, P + R0 / n_rep - window + 1) : 0;
-  const int tl0 = kmin / BN;
-  const int ntiles_all = kmax / BN + 1 - tl0;
-  const int per_split = (ntiles_all + nsplit - 1) / nsplit;
-  const int s_lo = min(split * per_split, ntiles_all);
-  const int t_lo = tl0 + s_lo;
-  const int ntiles = min(s_lo + per_split, ntiles_all) - s_lo;  // this workgroup's key tiles
+  // The rows and key range of the current work item (set_item).
+  int qt, R0, Rw, qtok, tok, head, w_tok_lo, w_tok_hi, key_lo, w_key_lo, w_mask_lo, t_lo, ntiles;
+  bool row_ok, wave_active;
+  auto set_item = [&](int q) {
+    qt = q;
+    R0 = qt * 128;
+    Rw = R0 + qblk * 32;
+    const int Rl = Rw + c32;
+    row_ok = Rl < rows_total;
+    qtok = row_ok ? Rl / n_rep : Tb - 1;      // token inside the chunk
+    tok = P + qtok;                           // its key position
+    head = g * n_rep + (row_ok ? Rl % n_rep : 0);
+    wave_active = Rw < rows_total;
+    w_tok_lo = P + min(Rw, rows_total - 1) / n_rep;
+    w_tok_hi = P + min(Rw + 31, rows_total - 1) / n_rep;
+    // Sliding window W (0: none): key position j is visible to the token at
+    // key position i iff i - W < j <= i.  key_lo is this lane's first visible
+    // key; keys below w_mask_lo are masked for at least one row of the wave.
+    key_lo = window > 0 ? tok - window + 1 : 0;
+    w_key_lo = window > 0 ? w_tok_lo - window + 1 : 0;
+    w_mask_lo = window > 0 ? w_tok_hi - window + 1 : 0;
+    // Key tiles of the item: from the first key its first row sees to the
+    // last key its last row sees.
+    const int kmax = P + min(R0 + 127, rows_total - 1) / n_rep;
+    const int kmin = window > 0 ? max(0, P + R0 / n_rep - window + 1) : 0;
+    const int tl0 = kmin / BN;
+    const int ntiles_all = kmax / BN + 1 - tl0;
+    const int per_split = (ntiles_all + nsplit - 1) / nsplit;
+    const int s_lo = min(split * per_split, ntiles_all);
+    t_lo = tl0 + s_lo;
+    ntiles = min(s_lo + per_split, ntiles_all) - s_lo;  // this workgroup's key tiles
+  };
+  set_item(qt_of(0));
 
   // Q^T fragments for the whole d_head, kept in VGPRs.
   typename MF::frag qf[DSTEPS];
-  {
+  auto load_q = [&]() {
     const T* qrow = Q + ((size_t)(q0 + qtok) * n_q + head) * kHeadDim + hk * MF::KL;
 #pragma unroll
     for (int ks = 0; ks < DSTEPS; ++ks) qf[ks] = row_ok ? MF::load(qrow + ks * MF::K) : MF::zero();
-  }
+  };
+  load_q();
 
   // Each key tile lies inside one cache block (paged block sizes are powers
   // of two >= 64), so one row lookup per tile addresses all its rows.
@@ -248,19 +264,22 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     }
   };
 
-  f32x16_v o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16_v{};
   // m_run: the reference max of the (log2-scaled) scores, at most kMaxSlack
   // below their running max (see the rescale below), -inf until this lane has
   // seen a key.  The score accumulators start at -m_run (0 while m_run is
-  // -inf), so they come out of the MFMAs already relative to it.
-  float m_run = FIXED ? fixed_ref : -INFINITY, l_run = 0.f;
-  f32x16_v mbias = f32x16_v{};
-  if constexpr (FIXED) {
+  // -inf), so they come out of the MFMAs already relative to it.  Reset for
+  // every work item.
+  f32x16_v o[4];
+  float m_run, l_run;
+  f32x16_v mbias;
+  auto reset_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mbias[i] = -fixed_ref;
-  }
+    for (int db = 0; db < 4; ++db) o[db] = f32x16_v{};
+    m_run = FIXED ? fixed_ref : -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mbias[i] = FIXED ? -fixed_ref : 0.f;
+  };
 
   // One key tile from stage P (0 or 1, a compile-time constant) of this
   // wave's key half.
@@ -463,22 +482,29 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   };
 
   // Key halves: half 0 takes tiles [0, n0), half 1 tiles [n0, ntiles).  Each
-  // half has two LDS stages (kh*2, kh*2+1) fed from two register sets: tile
-  // i+2's global loads are issued while tile i runs, and tile i+1 (loaded one
-  // iteration earlier) is staged after it.  Both halves run n0 iterations so
-  // every wave meets every barrier.
-  // (uniform; read from the first lane so the loop control stays scalar)
-  const int n0 = __builtin_amdgcn_readfirstlane(KSPLIT == 2 ? (ntiles + 1) / 2 : ntiles);
-  const int base = __builtin_amdgcn_readfirstlane(t_lo + (kh ? n0 : 0));
-  const int cnt = __builtin_amdgcn_readfirstlane(kh ? ntiles - n0 : n0);
+  // half has two LDS stages (kh*2, kh*2+1).  Both halves run n0 iterations
+  // so every wave meets every barrier.  (n0, base, cnt are uniform; read from
+  // the first lane so the loop control stays scalar.)
+  int n0, base, cnt;
+  auto set_range = [&]() {
+    n0 = __builtin_amdgcn_readfirstlane(KSPLIT == 2 ? (ntiles + 1) / 2 : ntiles);
+    base = __builtin_amdgcn_readfirstlane(t_lo + (kh ? n0 : 0));
+    cnt = __builtin_amdgcn_readfirstlane(kh ? ntiles - n0 : n0);
+  };
+  set_range();
   const int s0 = kh * 2, s1 = kh * 2 + 1;
+  if constexpr (VT) {
+    if (cnt > 0) dma_tile(base, s0);
+  }
+
+  for (int item = 0; item < items; ++item) {
+  reset_acc();
   if constexpr (VT) {
     // Two LDS stages per key half: tile i+1's loads are issued before tile i
     // runs into the stage that tile i-1 used (free once every wave passed the
-    // barrier that ended tile i-1).  Both halves run n0 iterations so every
-    // wave meets every barrier.
+    // barrier that ended tile i-1).
     // Unrolled by two so that each copy reads a fixed stage: tile i sits in
-    // stage i % 2 of the half.
+    // stage i % 2 of the half.  Tile 0 was issued before the item began.
     auto step = [&](int i, auto stage) {
       constexpr int P = decltype(stage)::value;
       if (i + 1 < cnt) dma_tile(base + i + 1, P ? s0 : s1);
@@ -486,7 +512,6 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i+1 has landed
       lds_barrier();
     };
-    if (cnt > 0) dma_tile(base, s0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and tile 0
     lds_barrier();
     for (int i = 0; i < n0; i += 2) {
@@ -505,6 +530,12 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     }
   }
 
+  // The current item's output rows (set_item moves on to the next item
+  // before they are stored).
+  const int o_qtok = qtok, o_head = head;
+  const bool o_ok = row_ok;
+  const bool more = item + 1 < items;
+
   // Merge the two key halves: half 1 hands (O, m, l) to half 0 through LDS,
   // as [block][register][lane] so every access is one contiguous row.
   if constexpr (KSPLIT == 2) {
@@ -517,8 +548,12 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     comb[64 * 64 + lane] = m_run;
     comb[65 * 64 + lane] = l_run;
   }
+  if (more) {  // the next item's Q fragments (qf is free once the key loop is done)
+    set_item(qt_of(item + 1));
+    load_q();
+  }
   lds_barrier();
-  if (kh == 1) return;
+  if (kh == 0) {
   if constexpr (FIXED) {
     // both halves are relative to the same reference: plain sums
     l_run += comb[65 * 64 + lane];
@@ -539,12 +574,29 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
       for (int i = 0; i < 16; ++i) o[db][i] = a0 * o[db][i] + a1 * comb[(db * 16 + i) * 64 + lane];
   }
   }
+  if (more) {
+    // comb has been read: the next item's first tiles may land in LDS while
+    // this item's rows are normalised and stored.
+    lds_barrier();
+    set_range();
+    if constexpr (VT) {
+      if (cnt > 0) dma_tile(base, s0);
+    }
+  }
+  } else if (more) {
+    set_item(qt_of(item + 1));
+    load_q();
+    set_range();
+    if constexpr (VT) {
+      if (cnt > 0) dma_tile(base, s0);
+    }
+  }
 
-  if (!row_ok) return;
+  if (kh == 0 && o_ok) {
   l_run += __shfl_xor(l_run, 32, kWave);
   if (nsplit > 1) {
     // Partial results of this key range: O unnormalised, and (m, l).
-    const size_t prow = ((size_t)split * n_tok + q0 + qtok) * n_q + head;
+    const size_t prow = ((size_t)split * n_tok + q0 + o_qtok) * n_q + o_head;
     float* po = part + prow * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -559,10 +611,9 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
       pml[0] = m_run;
       pml[1] = l_run;
     }
-    return;
-  }
+  } else {
   const float inv = 1.f / l_run;
-  T* orow = Out + ((size_t)(q0 + qtok) * n_q + head) * kHeadDim;
+  T* orow = Out + ((size_t)(q0 + o_qtok) * n_q + o_head) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -578,6 +629,9 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
         *reinterpret_cast<f32x4_v*>(orow + d) = w;
       }
     }
+  }
+  }
+  }  // work items
 }
 
 // Merge the nsplit partial results of each (token, query head): one online
@@ -635,14 +689,21 @@ static void launch_flash_kernel(int wgs, const T* Q, const T* Kc, const T* Vc, T
   // Few workgroups: split each query tile's key range over two wave groups
   // so both waves of a SIMD serve the same tile.  Many: 4-wave workgroups,
   // two resident per CU.
-  if (wgs < 4 * 256)
-    hipLaunchKernelGGL((flash_prefill_kernel<T, 2, FIXED>), dim3(wgs), dim3(512), 0, s, Q, Kc, Vc,
-                       Out, B, T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part,
-                       fixed_ref);
-  else
+  if (wgs < 4 * 256) {
+    // bf16 with whole 128-row query tiles, an even number of them per group
+    // and no key-range split: pair the heavy and light tiles, two work items
+    // per workgroup (the second one's loads overlap the first one's merge).
+    const int rows = T_len * (n_q / n_kv);
+    const int items =
+        (sizeof(T) == 2 && nsplit == 1 && !cu_seqlens && rows % 256 == 0) ? 2 : 1;
+    hipLaunchKernelGGL((flash_prefill_kernel<T, 2, FIXED>), dim3(wgs / items), dim3(512), 0, s, Q,
+                       Kc, Vc, Out, B, T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window,
+                       nsplit, part, fixed_ref, items);
+  } else {
     hipLaunchKernelGGL((flash_prefill_kernel<T, 1, FIXED>), dim3(wgs), dim3(256), 0, s, Q, Kc, Vc,
                        Out, B, T_len, cu_seqlens, n_tok, n_q, n_kv, kv, past, window, nsplit, part,
-                       fixed_ref);
+                       fixed_ref, 1);
+  }
 }
 
 template <typename T>
