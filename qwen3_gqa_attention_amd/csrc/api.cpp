@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstring>
@@ -96,7 +97,11 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
   }
   if (T != 1 || cap <= 0 || cap > INT_MAX) return false;
   const int chunk = q3::decode_chunk_keys();
-  const int64_t nchunk = (cap + chunk - 1) / chunk;
+  // partial slots per (sequence, KV head): every chunk of the cache, or with a
+  // sliding window only the chunks one window can overlap
+  int64_t nchunk = (cap + chunk - 1) / chunk;
+  if (d->sliding_window > 0)
+    nchunk = std::min<int64_t>(nchunk, ((int64_t)d->sliding_window + chunk - 1) / chunk + 1);
   const size_t n_rep = d->n_q / d->n_kv;
   const size_t slots = (size_t)n * d->n_kv * nchunk * n_rep;
   const size_t qb = align_up((size_t)n * hq * es);

@@ -187,7 +187,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     }
   }
   __syncthreads();
-  const size_t slot = ((size_t)(s * n_kv + g) * nchunk + c) * NREP;
+  // partial slot: the chunk's index inside the launched span (with a window
+  // the span starts at the chunk holding the first visible key)
+  const size_t slot = ((size_t)(s * n_kv + g) * nchunk + blockIdx.x) * NREP;
   for (int idx = tid; idx < NREP * kHeadDim; idx += 256) {
     const int r = idx / kHeadDim, d = idx % kHeadDim;
     float M = -INFINITY;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + NW * u;
-      const size_t sl = (base + c) * n_rep + r;
+      const size_t sl = (base + (c - c_lo)) * n_rep + r;
       const bool ok = c < nc;
       mv[u] = ok ? part_ml[sl * 2] : -INFINITY;
       lv[u] = ok ? part_ml[sl * 2 + 1] : 0.f;
@@ -291,8 +293,9 @@ static void launch_decode_nrep(const T* Q, const T* Kc, const T* Vc, const int32
                                int N, int n_q, int n_kv, const KvAddr& kv, int window,
                                const DecodeScratch& ws, hipStream_t s) {
   // a window of W keys overlaps at most ceil(W / chunk) + 1 chunks
-  const int gx = window > 0 ? std::min(ws.nchunk, (window + kDecodeChunk - 1) / kDecodeChunk + 1)
-                            : ws.nchunk;
+  // ws.nchunk chunks per (sequence, KV head): all of the cache, or with a
+  // window of W keys the ceil(W / chunk) + 1 chunks it can overlap
+  const int gx = ws.nchunk;
   hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(gx, n_kv, N), dim3(256), 0, s, Q,
                      Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, kv, ws.nchunk, window);
 }

@@ -136,7 +136,8 @@ size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv, int n_tok);
 struct DecodeScratch {
   float* part_acc;  // [N, n_kv, nchunk, n_rep, 128]
   float* part_ml;   // [N, n_kv, nchunk, n_rep, 2]
-  int nchunk;
+  int nchunk;       // chunks launched per (sequence, KV head): all of the cache, or with a
+                    // window the ceil(W / chunk) + 1 it can overlap (slot = index in that span)
   int chunk;
 };
 int decode_chunk_keys();
