@@ -120,10 +120,19 @@ def test_varlen_workspace_size(built_lib):
         assert q3.qwen3_attn_workspace_size_varlen(d, *args) == 0, args
 
 
-def test_sliding_window_leaves_the_workspace_unchanged(built_lib):
-    for args in ((0, 2, 2048, 0), (0, 1, 128, 0), (1, 64, 1, 32832)):
+def test_sliding_window_workspace(built_lib):
+    # prefill: unchanged by the window
+    for args in ((0, 2, 2048, 0), (0, 1, 128, 0)):
         assert (q3.qwen3_attn_workspace_size(desc(sliding_window=4096), *args)
                 == q3.qwen3_attn_workspace_size(desc(), *args) > 0)
+    # decode: partial slots for the ceil(W / 512) + 1 chunks a window can overlap,
+    # never more than the whole cache needs
+    full = q3.qwen3_attn_workspace_size(desc(), 1, 64, 1, 32832)
+    win = q3.qwen3_attn_workspace_size(desc(sliding_window=4096), 1, 64, 1, 32832)
+    assert 0 < win < full
+    for W in (1, 512, 513, 32832, 100000):
+        assert 0 < q3.qwen3_attn_workspace_size(desc(sliding_window=W), 1, 64, 1, 32832) <= full
+    assert (q3.qwen3_attn_workspace_size(desc(sliding_window=100000), 1, 64, 1, 32832) == full)
 
 
 def test_varlen_rejects_missing_offsets_and_inconsistent_sizes(built_lib):
