@@ -93,7 +93,8 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   // Two key halves x two stages of K and V tiles; after the key loop the
   // same memory carries the second half's partial results to the first.
   constexpr int KSZ = BN * LDK;
-  constexpr int COMB = 4 * 66 * 64 * 4 / sizeof(T);   // 4 blocks x (64 O + m + l) x 64 lanes, fp32
+  // merge area: 4 query blocks x 64 lanes x (64 O + m + l, padded to 68), fp32
+  constexpr int COMB = 4 * 64 * 68 * 4 / sizeof(T);
   constexpr int SMEM = 2 * KSPLIT * (KSZ + VSZ) > COMB ? 2 * KSPLIT * (KSZ + VSZ) : COMB;
   __shared__ __attribute__((aligned(16))) T smem[SMEM];
   auto Ks = [&](int st) { return smem + st * KSZ; };
@@ -542,21 +543,24 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
 
   // The current item's output rows (set_item moves on to the next item
   // before they are stored).
-  const int o_qtok = qtok, o_head = head;
+  const int o_qtok = qtok, o_head = head, o_Rw = __builtin_amdgcn_readfirstlane(Rw);
   const bool o_ok = row_ok;
   const bool more = item + 1 < items;
 
   // Merge the two key halves: half 1 hands (O, m, l) to half 0 through LDS,
-  // as [block][register][lane] so every access is one contiguous row.
+  // each lane's 66 values contiguous (rows of 68 floats: the 16-byte accesses
+  // of 16 consecutive lanes hit distinct banks), so both sides move them with
+  // 16-byte LDS instructions.
   if constexpr (KSPLIT == 2) {
-  float* comb = reinterpret_cast<float*>(smem) + qblk * 66 * 64;
+  float* comb = reinterpret_cast<float*>(smem) + (qblk * 64 + lane) * 68;
   if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) comb[(db * 16 + i) * 64 + lane] = o[db][i];
-    comb[64 * 64 + lane] = m_run;
-    comb[65 * 64 + lane] = l_run;
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4_v*>(comb + db * 16 + i4 * 4) =
+            f32x4_v{o[db][i4 * 4], o[db][i4 * 4 + 1], o[db][i4 * 4 + 2], o[db][i4 * 4 + 3]};
+    *reinterpret_cast<f32x2_v*>(comb + 64) = f32x2_v{m_run, l_run};
   }
   if (more) {  // the next item's Q fragments (qf is free once the key loop is done)
     set_item(qt_of(item + 1));
@@ -566,13 +570,21 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
   if (kh == 0) {
   if constexpr (FIXED) {
     // both halves are relative to the same reference: plain sums
-    l_run += comb[65 * 64 + lane];
+    l_run += comb[65];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
+    {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] += comb[(db * 16 + i) * 64 + lane];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4_v c = *reinterpret_cast<const f32x4_v*>(comb + db * 16 + i4 * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[db][i4 * 4 + e] += c[e];
+      }
+      // one block's 16 values in flight at a time (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+    }
   } else {
-    const float m1 = comb[64 * 64 + lane], l1 = comb[65 * 64 + lane];
+    const float m1 = comb[64], l1 = comb[65];
     const float M = fmaxf(m_run, m1);
     const float a0 = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
     const float a1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - M);
@@ -580,8 +592,15 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     m_run = M;  // O and l are now relative to the merged max (the split path writes it)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
+    {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] = a0 * o[db][i] + a1 * comb[(db * 16 + i) * 64 + lane];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4_v c = *reinterpret_cast<const f32x4_v*>(comb + db * 16 + i4 * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[db][i4 * 4 + e] = a0 * o[db][i4 * 4 + e] + a1 * c[e];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   }
   if (more) {
@@ -602,43 +621,97 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
     }
   }
 
-  if (kh == 0 && o_ok) {
+  if (kh == 0) {
+  // (the two lanes of a row have the same o_ok, so the exchange is within
+  // valid or within invalid rows)
   l_run += __shfl_xor(l_run, 32, kWave);
   if (nsplit > 1) {
-    // Partial results of this key range: O unnormalised, and (m, l).
-    const size_t prow = ((size_t)split * n_tok + q0 + o_qtok) * n_q + o_head;
-    float* po = part + prow * kHeadDim;
+    if (o_ok) {
+      // Partial results of this key range: O unnormalised, and (m, l).
+      const size_t prow = ((size_t)split * n_tok + q0 + o_qtok) * n_q + o_head;
+      float* po = part + prow * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = db * 32 + 8 * i4 + 4 * hk;
+          *reinterpret_cast<f32x4_v*>(po + d) =
+              f32x4_v{o[db][i4 * 4 + 0], o[db][i4 * 4 + 1], o[db][i4 * 4 + 2], o[db][i4 * 4 + 3]};
+        }
+      if (hk == 0) {
+        float* pml = part + (size_t)nsplit * n_tok * n_q * kHeadDim + prow * 2;
+        pml[0] = m_run;
+        pml[1] = l_run;
+      }
+    }
+  } else if constexpr (VT && KSPLIT == 2) {
+    // The wave's 32 rows leave through LDS so that every store is a whole
+    // 16-byte piece of a row (one instruction covers 4 rows; storing from
+    // the accumulator layout takes 16 instructions of 32 scattered 16-byte
+    // pieces each): 0.6B attention 46.7 -> 45.6 us.  (The 4-wave variant
+    // keeps the direct stores: there the extra registers cost more, 4B
+    // attention 133.2 -> 135.3 us.)  8 KB per wave, in stages that neither
+    // the merge area nor the next item's first tiles use; the next item
+    // loads into them only after the barrier that starts its key loop.  Row
+    // r keeps its 16-byte chunk c at c ^ (r & 15) (conflict-free on both
+    // sides).
+    const float inv = 1.f / l_run;
+    T* ost = Vs(qblk < 2 ? 1 : 3) + (qblk & 1) * 32 * kHeadDim;
+    // this lane's row and swizzle, formed here (an opaque value, so the
+    // compiler does not precompute the addresses and hold them through the
+    // key loop)
+    int wrow = c32;
+    asm volatile("" : "+v"(wrow));
+    T* wst = ost + wrow * kHeadDim + 4 * hk;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const u32x2_v w{pack_bf16x2(o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv),
+                        pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv)};
+        *reinterpret_cast<u32x2_v*>(wst + (((db * 4 + i4) ^ (wrow & 15)) * 8)) = w;
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    int ch = lane & 15, lr = lane >> 4;
+    asm volatile("" : "+v"(ch), "+v"(lr));
+    // rows o_Rw + r, r = 4 it + lane / 16: token and head advance by whole
+    // steps of 4 rows (n_rep divides n_q; no division per store)
+    int R = o_Rw + lr;
+    int tk = R / n_rep, rm = R - tk * n_rep;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 4 + lr;
+      const u32x4_v v = ld16(ost + r * kHeadDim + ((ch ^ (r & 15)) * 8));
+      if (R < rows_total)
+        st16(Out + ((size_t)(q0 + tk) * n_q + g * n_rep + rm) * kHeadDim + ch * 8, v);
+      R += 4;
+      rm += 4;
+      while (rm >= n_rep) {
+        rm -= n_rep;
+        ++tk;
+      }
+      if (it == 3) __builtin_amdgcn_sched_barrier(0);  // four rows' loads in flight at a time
+    }
+  } else if (o_ok) {
+    const float inv = 1.f / l_run;
+    T* orow = Out + ((size_t)(q0 + o_qtok) * n_q + o_head) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + 8 * i4 + 4 * hk;
-        *reinterpret_cast<f32x4_v*>(po + d) =
-            f32x4_v{o[db][i4 * 4 + 0], o[db][i4 * 4 + 1], o[db][i4 * 4 + 2], o[db][i4 * 4 + 3]};
+        if constexpr (VT) {
+          const u32x2_v w{pack_bf16x2(o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv),
+                          pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv)};
+          *reinterpret_cast<u32x2_v*>(orow + d) = w;
+        } else {
+          const f32x4_v w{o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv,
+                          o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv};
+          *reinterpret_cast<f32x4_v*>(orow + d) = w;
+        }
       }
-    if (hk == 0) {
-      float* pml = part + (size_t)nsplit * n_tok * n_q * kHeadDim + prow * 2;
-      pml[0] = m_run;
-      pml[1] = l_run;
-    }
-  } else {
-  const float inv = 1.f / l_run;
-  T* orow = Out + ((size_t)(q0 + o_qtok) * n_q + o_head) * kHeadDim;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = db * 32 + 8 * i4 + 4 * hk;
-      if constexpr (VT) {
-        u32x2_v w{pack_bf16x2(o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv),
-                  pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv)};
-        *reinterpret_cast<u32x2_v*>(orow + d) = w;
-      } else {
-        f32x4_v w{o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv, o[db][i4 * 4 + 2] * inv,
-                  o[db][i4 * 4 + 3] * inv};
-        *reinterpret_cast<f32x4_v*>(orow + d) = w;
-      }
-    }
   }
   }
   }  // work items
