@@ -538,8 +538,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="run only the prefill step and the full-attention decode (the two "
                          "roofline kernels), e.g. under a profiler")
-    ap.add_argument("--only", choices=["4b", "wide-gqa", "chunk"],
-                    help="time one secondary prefill workload alone and print its own JSON line "
+    ap.add_argument("--only", choices=["4b", "wide-gqa", "chunk", "decode", "decode-window"],
+                    help="time one secondary workload alone and print its own JSON line "
                          "(for profiling it by itself; not the headline line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy of known size (for PMC traffic calibration)")
@@ -567,6 +567,15 @@ def main():
     if args.only:
         if args.only == "chunk":
             r = bench_chunk(args)
+        elif args.only.startswith("decode"):
+            W = 4096 if args.only == "decode-window" else 0
+            dd = bench_decode(args, window=W)
+            nbytes = dd["kv_read"] + dd["weights"]
+            r = {"workload": dd["w"].name + (f"-window{W}" if W else ""), "window": W,
+                 "steps": args.decode_steps, "ms_per_step": dd["step_s"] * 1e3,
+                 "GBps": nbytes / dd["step_s"] / 1e9,
+                 "frac_hbm_peak": nbytes / dd["step_s"] / PEAK_HBM_BYTES,
+                 "kernel_ms": dict(zip(q3.STAGES, dd["stage_ms"]))}
         else:
             pc = bench_prefill(args, idx=3 if args.only == "4b" else 4, steps="duration")
             r = {"workload": pc["w"].name, "B": pc["B"], "T": pc["T"], "steps": pc["steps"],

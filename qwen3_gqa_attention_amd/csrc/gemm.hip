@@ -347,12 +347,12 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
   int head = 0, kind = 3;  // kind 3: plain projection output
   // 256x256 q/k/v tiles: the two waves of a row block share the RoPE angles
   constexpr bool kShareAngles = QKV && WN == 2 && KG == 1;
-  const bool share = kShareAngles && (n0 >> 7) < qe.n_q + qe.n_kv;
+  const bool share = kShareAngles && qe.head0 + (n0 >> 7) < qe.n_q + qe.n_kv;
   static_assert(!kShareAngles || WM * MI * 16 * 64 * 16 <= SMEM * (int)sizeof(T), "angles do not fit");
   if constexpr (QKV) {
-    // This wave's 128 columns are head (n0/128 + wn): [0, n_q) query heads,
+    // This wave's 128 columns are head head0 + n0/128 + wn: [0, n_q) query heads,
     // then n_kv key heads, then n_kv value heads.
-    head = (n0 >> 7) + wn;
+    head = qe.head0 + (n0 >> 7) + wn;
     kind = head < qe.n_q ? 0 : (head < qe.n_q + qe.n_kv ? 1 : 2);
     if constexpr (kShareAngles) {
       // The tile's two waves of a row block need the same (row, frequency)
@@ -668,10 +668,32 @@ hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const
     // 256x256 tiles unless their last round leaves many CUs idle: one tile
     // per CU per round, each round costing a fixed ~15 us (prologue,
     // epilogue, stores) plus the main loop, which is half as long for a
-    // 256x128 tile (measured on the 0.6B, 4B and wide-GQA shapes).
+    // 256x128 tile (measured on the 0.6B, 4B and wide-GQA shapes).  A third
+    // choice covers whole rounds with 256x256 tiles and the remaining
+    // columns with 256x128 tiles in a second launch (e.g. the 4B shape:
+    // one round of each instead of 1.5 rounds of 256x256 or 3 of 256x128).
     const float k = (float)K;
-    const float c256 = (float)((t256 + kCus - 1) / kCus) * (15.f + 0.0245f * k);
-    const float c128 = (float)((t128 + kCus - 1) / kCus) * (15.f + 0.0125f * k);
+    const float r256 = 15.f + 0.0245f * k, r128 = 15.f + 0.0125f * k;
+    const int mt = (M + 255) / 256;
+    const float c256 = (float)((t256 + kCus - 1) / kCus) * r256;
+    const float c128 = (float)((t128 + kCus - 1) / kCus) * r128;
+    const int n1 = (t256 / kCus) * kCus / mt;  // 256-column tiles in whole rounds
+    const int t_rest = mt * ((N - n1 * 256) / 128);
+    const float cmix = (n1 > 0 && n1 * 256 < N)
+                           ? (float)((mt * n1 + kCus - 1) / kCus) * r256 +
+                                 (float)((t_rest + kCus - 1) / kCus) * r128
+                           : 1e30f;
+    if (cmix < c256 && cmix < c128) {
+      const int N1 = n1 * 256;
+      QkvEpilogue e2 = e;
+      e2.head0 = e.head0 + N1 / kHeadDim;
+      hipError_t r = norm ? launch_gemm<T, 4, 2, 2, 4, true, false, 2, true>(X, Wqkv, M, N1, K, e, se, s)
+                          : launch_gemm<T, 4, 2, 2, 4, true>(X, Wqkv, M, N1, K, e, se, s);
+      if (r != hipSuccess) return r;
+      const T* W2 = Wqkv + (size_t)N1 * K;
+      return norm ? launch_gemm<T, 8, 1, 1, 4, true, false, 2, true>(X, W2, M, N - N1, K, e2, se, s)
+                  : launch_gemm<T, 8, 1, 1, 4, true>(X, W2, M, N - N1, K, e2, se, s);
+    }
     if (c256 <= c128)
       return norm ? launch_gemm<T, 4, 2, 2, 4, true, false, 2, true>(X, Wqkv, M, N, K, e, se, s)
                   : launch_gemm<T, 4, 2, 2, 4, true>(X, Wqkv, M, N, K, e, se, s);

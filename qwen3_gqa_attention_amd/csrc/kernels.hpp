@@ -57,6 +57,8 @@ struct QkvEpilogue {
                              // sequence s owns rows cu[s] .. cu[s+1]-1 (slot = past[s] +
                              // row - cu[s]); null: rows_per_seq rows each
   int nseq;
+  int head0;                 // head of the launch's first column (a launch may cover a
+                             // column range of the merged q/k/v projection)
 
   // Sequence and cache slot of projection row `row` (prefill and decode).
   __device__ __forceinline__ void seq_slot(int row, int* seq, int* slot) const {
