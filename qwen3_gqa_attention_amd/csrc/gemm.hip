@@ -516,8 +516,126 @@ static int small_m_ksplit(int N, int K) {
 }
 
 int small_m_partial_floats(int M, int N, int K, int es) {
-  const int ks = es == 2 ? small_m_ksplit<bf16_t>(N, K) : small_m_ksplit<float>(N, K);
+  // bf16: one unsplit fp32 product (the skinny kernel below); fp32: the slices
+  const int ks = es == 2 ? 1 : small_m_ksplit<float>(N, K);
   return ks * M * N;
+}
+
+// ---------------------------------------------------------------------------
+// Decode-sized bf16 projection without a K split over the grid: workgroup b
+// owns a BM x BN block of C = A W^T over the whole of K, and its eight waves
+// each take a contiguous eighth of K, then add their blocks through LDS.
+// There is no LDS staging of the operands: each lane loads its 16x16x32 MFMA
+// fragments (row or column l % 16, 8 consecutive k at 8 * (l / 16) of a
+// 32-k step) straight from global memory, KW steps' worth at a time, so a
+// CU has 128 KB of loads in flight at once -- the weights are read once,
+// and the block's rows of A come from L2.  Blocks are numbered column block
+// fastest; with a multiple of 8 column blocks every row block of a column
+// block lands on the same XCD (workgroups go to XCDs round-robin), so its
+// slab of W is fetched from HBM into one L2 once.
+//   16x16x32 MFMA: lane l holds D row 4 * (l / 16) + i, column l % 16.
+// Output: fp32 to Cf (row stride N), or, when Cf is null, T to Cb plus the
+// optional residual (same layout), rounded once.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int KW>
+__global__ __launch_bounds__(512) void skinny_gemm_kernel(const bf16_t* __restrict__ A,
+                                                          const bf16_t* __restrict__ W, int M,
+                                                          int N, int K, float* __restrict__ Cf,
+                                                          bf16_t* __restrict__ Cb,
+                                                          const bf16_t* __restrict__ residual) {
+  constexpr int RB = BM / 16, CB = BN / 16;
+  const int ncb = N / BN;
+  const int cb0 = blockIdx.x % ncb, rb0 = blockIdx.x / ncb;
+  const int m0 = rb0 * BM, n0 = cb0 * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  // this wave's 32-k steps: a contiguous range
+  const int nsteps = K / 32;
+  const int spw = (nsteps + 7) / 8;
+  const int s_beg = min(wave * spw, nsteps), s_end = min(s_beg + spw, nsteps);
+  const bf16_t* ap[RB];
+  const bf16_t* wp[CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) ap[i] = A + (size_t)min(m0 + 16 * i + r16, M - 1) * K + kq;
+#pragma unroll
+  for (int j = 0; j < CB; ++j) wp[j] = W + (size_t)(n0 + 16 * j + r16) * K + kq;
+  f32x4_v acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = s_beg; s0 < s_end; s0 += KW) {
+    bf16x8_v af[KW][RB], wf[KW][CB];
+    // every load of the chunk first (steps past the range re-read the last
+    // one and are zeroed, so the count stays fixed)
+#pragma unroll
+    for (int u = 0; u < KW; ++u) {
+      const int k = min(s0 + u, s_end - 1) * 32;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) af[u][i] = *reinterpret_cast<const bf16x8_v*>(ap[i] + k);
+#pragma unroll
+      for (int j = 0; j < CB; ++j) wf[u][j] = *reinterpret_cast<const bf16x8_v*>(wp[j] + k);
+    }
+    // keep the scheduler from sinking loads between the MFMAs (it would
+    // reuse their registers and leave only a few in flight)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < KW; ++u) {
+      if (s0 + u >= s_end) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) af[u][i] = bf16x8_v{};
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][i], wf[u][j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // sum of the eight waves' blocks
+  __shared__ f32x4_v red[8][RB * CB][64];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) red[wave][i * CB + j][lane] = acc[i][j];
+  __syncthreads();
+  for (int q = threadIdx.x; q < RB * CB * 64; q += 512) {
+    const int blk = q >> 6, l = q & 63;
+    f32x4_v v = red[0][blk][l];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) v += red[w][blk][l];
+    const int col = n0 + (blk % CB) * 16 + (l & 15);
+    const int rowb = m0 + (blk / CB) * 16 + 4 * (l >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = rowb + e;
+      if (row >= M) break;
+      const size_t o = (size_t)row * N + col;
+      if (Cf) {
+        Cf[o] = v[e];
+      } else {
+        const float r = residual ? bf16_to_f32(residual[o]) : 0.f;
+        Cb[o] = f32_to_bf16(v[e] + r);
+      }
+    }
+  }
+}
+
+// Launch of the skinny kernel: 32x32 blocks when they alone give a workgroup
+// per CU, else 16x16 (e.g. o_proj of 64 rows, 1024 columns: 256 blocks).
+// Each lane keeps 16 fragments (64 VGPRs) in flight per chunk.
+static hipError_t launch_skinny(const bf16_t* A, const bf16_t* W, int M, int N, int K, float* Cf,
+                                bf16_t* Cb, const bf16_t* residual, hipStream_t s) {
+  const int t32 = ((M + 31) / 32) * (N / 32);
+  if (N % 32 == 0 && t32 >= 256) {
+    hipLaunchKernelGGL((skinny_gemm_kernel<32, 32, 4>), dim3(t32), dim3(512), 0, s, A, W, M, N, K,
+                       Cf, Cb, residual);
+  } else {
+    const int t16 = ((M + 15) / 16) * (N / 16);
+    hipLaunchKernelGGL((skinny_gemm_kernel<16, 16, 8>), dim3(t16), dim3(512), 0, s, A, W, M, N, K,
+                       Cf, Cb, residual);
+  }
+  return hipGetLastError();
 }
 
 // Sum the K-slice partials of the q/k/v projection for one head (128
@@ -651,9 +769,15 @@ hipError_t launch_qkv_gemm(const T* X, const T* Wqkv, int M, int N, int K, const
                            hipStream_t s, float* part) {
   StoreEpilogue se{nullptr, 0, nullptr};
   if (M <= kSmallM && part) {
-    const int ks = small_m_ksplit<T>(N, K);
-    StoreEpilogue ps{part, N, nullptr};
-    hipError_t r = launch_gemm<T, 2, 1, 1, 4, false, true>(X, Wqkv, M, N, K, e, ps, s, ks);
+    int ks = 1;
+    hipError_t r;
+    if constexpr (sizeof(T) == 2) {
+      r = launch_skinny(X, Wqkv, M, N, K, part, nullptr, nullptr, s);
+    } else {
+      ks = small_m_ksplit<T>(N, K);
+      StoreEpilogue ps{part, N, nullptr};
+      r = launch_gemm<T, 2, 1, 1, 4, false, true>(X, Wqkv, M, N, K, e, ps, s, ks);
+    }
     if (r != hipSuccess) return r;
     hipLaunchKernelGGL(qkv_finish_kernel<T>, dim3(N / kHeadDim, (M + 15) / 16), dim3(256), 0, s,
                        part, ks, M, N, K, e);
@@ -717,6 +841,9 @@ hipError_t launch_proj_gemm(const T* A, const T* W, T* C, int M, int N, int K, h
   QkvEpilogue qe{};
   StoreEpilogue se{C, N, residual};
   const bool res = residual != nullptr;
+  if constexpr (sizeof(T) == 2) {
+    if (M <= kSmallM) return launch_skinny(A, W, M, N, K, nullptr, C, residual, s);
+  }
   if (M <= kSmallM && part) {
     const int ks = small_m_ksplit<T>(N, K);
     StoreEpilogue ps{part, N, nullptr};

@@ -92,12 +92,25 @@ def test_workspace_size_prefill_and_decode(built_lib):
     cap, N = 32832, 64
     nchunk = -(-cap // 512)
     slots = N * 8 * nchunk * 2
-    # split-K partials of the 64-row projections (the fewest K slices giving
-    # at least 64 workgroups of 128 columns): q/k/v 2 slices x 64 x 4096,
-    # o_proj 8 slices x 64 x 1024 (fp32); the larger is reserved
-    part = max(2 * 64 * 4096, 8 * 64 * 1024) * 4
+    # bf16 64-row projections: the unsplit fp32 q/k/v product (64 x 4096) that
+    # the finishing kernel normalises (o_proj needs none)
+    part = 64 * 4096 * 4
     want = 2 * align(N * 2048 * 2) + align(slots * 128 * 4) + align(slots * 2 * 4) + align(part)
     assert q3.qwen3_attn_workspace_size(d, 1, N, 1, cap) == want
+    # fp32: split-K partials (the fewest K slices giving at least 64
+    # workgroups of 128 columns): q/k/v 2 slices x 64 x 4096, o_proj 8 x 64 x
+    # 1024; the larger is reserved
+    d32 = desc(dtype=q3.QWEN3_ATTN_F32)
+    part = max(2 * 64 * 4096, 8 * 64 * 1024) * 4
+    want = 2 * align(N * 2048 * 4) + align(slots * 128 * 4) + align(slots * 2 * 4) + align(part)
+    assert q3.qwen3_attn_workspace_size(d32, 1, N, 1, cap) == want
+    # a sliding window of W keys: partial slots for the ceil(W / 512) + 1
+    # chunks it can overlap
+    dw = desc(sliding_window=4096)
+    slots_w = N * 8 * 9 * 2
+    want = (2 * align(N * 2048 * 2) + align(slots_w * 128 * 4) + align(slots_w * 2 * 4)
+            + align(64 * 4096 * 4))
+    assert q3.qwen3_attn_workspace_size(dw, 1, N, 1, cap) == want
 
 
 @pytest.mark.parametrize("args", [(0, 0, 128, 0), (0, 2, 0, 0), (1, 4, 2, 100), (1, 4, 1, 0),
