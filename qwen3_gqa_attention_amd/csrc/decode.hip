@@ -107,28 +107,42 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
   }
 
-  const T* Kl = Kc + oct * 8;
-  const T* Vl = Vc + oct * 8;
   constexpr int U = kDecodeUnroll;
-  // Iterations stay on the 4U-key grid (one cache-block lookup each); keys
-  // below klo in the first one are masked.
-  for (int kb = max(wk0, klo & ~(4 * U - 1)); kb < wk1; kb += 4 * U) {
-    // The 4U keys from kb (a multiple of 4U) lie in one cache block.
-    const int64_t r0 = kv.row(s, g, kb);
-    RowSlice<T> kr[U], vr[U];
+  // One iteration: 4U keys from kb (a multiple of 4U, so they lie in one
+  // cache block: one block lookup).  Every lane loads a row; a key outside
+  // [klo, wk1) reads the row of key min(key, wk1 - 1) -- a visible or
+  // masked slot of the same block, never past the sequence's last key --
+  // and is then masked: score -inf, value row zero (a slot that was never
+  // written may hold NaN).
+  struct Rows {
+    RowSlice<T> k[U], v[U];
     bool val[U];
+  };
+  // Addresses: the iteration's first row as a wave-uniform base (scalar
+  // registers) plus a 32-bit byte offset per lane.
+  auto load = [&](Rows& b, int kb) {
+    const int64_t r0 = kv.row(s, g, kb);
+    const uint32_t r0lo = __builtin_amdgcn_readfirstlane((uint32_t)r0);
+    const uint32_t r0hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)r0 >> 32));
+    const uint64_t off0 = ((uint64_t)r0hi << 32 | r0lo) * (kHeadDim * sizeof(T));
+    const char* kbp = reinterpret_cast<const char*>(Kc) + off0;
+    const char* vbp = reinterpret_cast<const char*>(Vc) + off0;
+    const int lim = wk1 - 1 - kb;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = kb + grp + 4 * u;
-      val[u] = key < wk1 && key >= klo;
-      if (val[u]) {
-        kr[u].load_stream(Kl + (r0 + grp + 4 * u) * kHeadDim);
-        vr[u].load_stream(Vl + (r0 + grp + 4 * u) * kHeadDim);
-      } else {
-        kr[u].zero();
-        vr[u].zero();
-      }
+      b.val[u] = key < wk1 && key >= klo;
+      const uint32_t o = (uint32_t)(min(grp + 4 * u, lim) * kHeadDim + oct * 8) * sizeof(T);
+      b.k[u].load_stream(reinterpret_cast<const T*>(kbp + o));
+      b.v[u].load_stream(reinterpret_cast<const T*>(vbp + o));
     }
+  };
+  // One head at a time (16 heads: the scores of all heads would not fit in
+  // registers).
+  auto consume_per_head = [&](Rows& b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (!b.val[u]) b.v[u].zero();
 #pragma unroll
     for (int r = 0; r < NREP; ++r) {
       float sc[U];
@@ -137,9 +151,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
       for (int u = 0; u < U; ++u) {
         float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(q[r][e], kr[u].at(e), d);
+        for (int e = 0; e < 8; ++e) d = fmaf(q[r][e], b.k[u].at(e), d);
         d = row16_sum(d);
-        sc[u] = val[u] ? d : -INFINITY;
+        sc[u] = b.val[u] ? d : -INFINITY;
         mx = fmaxf(mx, sc[u]);
       }
       if (mx == -INFINITY) continue;  // uniform within the 16-lane group
@@ -154,8 +168,99 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
         const float p = __builtin_amdgcn_exp2f(sc[u] - m_new);
         l[r] += p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, vr[u].at(e), acc[r][e]);
+        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, b.v[u].at(e), acc[r][e]);
       }
+    }
+  };
+  // Keys outer, heads inner: each row is widened to fp32 once and used by
+  // all n_rep heads at once (per head, the compiler keeps every widened row
+  // live across the heads: 2 heads took 190 VGPRs instead of 139).
+  auto consume = [&](Rows& b) {
+    if constexpr (NREP > 8) {
+      consume_per_head(b);
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (!b.val[u]) b.v[u].zero();
+    float sc[NREP][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[e] = b.k[u].at(e);
+#pragma unroll
+      for (int r = 0; r < NREP; ++r) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(q[r][e], kf[e], d);
+        d = row16_sum(d);
+        sc[r][u] = b.val[u] ? d : -INFINITY;
+      }
+    }
+    float p[NREP][U];
+#pragma unroll
+    for (int r = 0; r < NREP; ++r) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[r][u]);
+      if (mx == -INFINITY) {  // uniform within the 16-lane group
+#pragma unroll
+        for (int u = 0; u < U; ++u) p[r][u] = 0.f;
+        continue;
+      }
+      const float m_new = fmaxf(m[r], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[r] - m_new);
+      m[r] = m_new;
+      l[r] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[r][u] = __builtin_amdgcn_exp2f(sc[r][u] - m_new);
+        l[r] += p[r][u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] = b.v[u].at(e);
+#pragma unroll
+      for (int r = 0; r < NREP; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p[r][u], vf[e], acc[r][e]);
+    }
+  };
+  // Iterations stay on the 4U-key grid; keys below klo in the first one are
+  // masked.  For 2..8 heads per KV head, two row buffers: the next
+  // iteration's loads are issued before the current one is consumed, so each
+  // wave keeps two iterations in flight (bf16, 2 heads: 139 VGPRs, three
+  // waves per SIMD, against 126 and four single-buffered: 48 against 32 KB
+  // in flight per SIMD).  One head already has eight waves per SIMD, and 16
+  // heads would spill.
+  constexpr bool kTwoBuffers = NREP >= 2 && NREP <= 8;
+  int kb = max(wk0, klo & ~(4 * U - 1));
+  if constexpr (!kTwoBuffers) {
+    for (; kb < wk1; kb += 4 * U) {
+      Rows b;
+      load(b, kb);
+      consume(b);
+    }
+  } else if (kb < wk1) {
+    Rows ba, bb;
+    load(ba, kb);
+    while (true) {
+      const bool more_b = kb + 4 * U < wk1;
+      if (more_b) load(bb, kb + 4 * U);
+      consume(ba);
+      if (!more_b) break;
+      kb += 4 * U;
+      const bool more_a = kb + 4 * U < wk1;
+      if (more_a) load(ba, kb + 4 * U);
+      consume(bb);
+      if (!more_a) break;
+      kb += 4 * U;
     }
   }
 
