@@ -62,6 +62,7 @@ qwen3_attn_status check_desc(const qwen3_attn_desc* d) {
 struct WsLayout {
   size_t q_off, a_off, acc_off, ml_off, part_off, total;
   int nchunk;
+  int chunk;  // decode: keys per chunk
   bool part;  // decode projections run split-K through the part region
 };
 
@@ -78,6 +79,7 @@ bool ws_layout_prefill(const qwen3_attn_desc* d, int32_t B, int32_t n_tok, int32
   L->a_off = qb;
   L->acc_off = L->ml_off = 0;
   L->nchunk = 0;
+  L->chunk = 0;
   L->part = false;
   L->part_off = 2 * qb;
   L->total = L->part_off +
@@ -96,7 +98,9 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
     return ws_layout_prefill(d, n, n * T, T, L);
   }
   if (T != 1 || cap <= 0 || cap > INT_MAX) return false;
-  const int chunk = q3::decode_chunk_keys();
+  // keys per chunk, from the most keys one (sequence, KV head) can see
+  const int64_t span = d->sliding_window > 0 ? std::min<int64_t>(cap, d->sliding_window) : cap;
+  const int chunk = q3::decode_chunk_keys(n, d->n_kv, span);
   // partial slots per (sequence, KV head): every chunk of the cache, or with a
   // sliding window only the chunks one window can overlap
   int64_t nchunk = (cap + chunk - 1) / chunk;
@@ -121,6 +125,7 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
   }
   L->total = L->part_off + align_up(part_floats * sizeof(float));
   L->nchunk = (int)nchunk;
+  L->chunk = chunk;
   return true;
 }
 
@@ -210,8 +215,7 @@ qwen3_attn_status run_decode(qwen3_attn_t* h, const void* hidden, const int32_t*
                                         e, s, part);
   if (r != hipSuccess) return QWEN3_ATTN_EHIP;
   q3::DecodeScratch sc{reinterpret_cast<float*>(ws + L.acc_off),
-                       reinterpret_cast<float*>(ws + L.ml_off), L.nchunk,
-                       q3::decode_chunk_keys()};
+                       reinterpret_cast<float*>(ws + L.ml_off), L.nchunk, L.chunk};
   mark(h, s, 1);
   r = q3::launch_decode_attn<T>(qbuf, reinterpret_cast<const T*>(k_cache),
                                 reinterpret_cast<const T*>(v_cache), positions, abuf, N, d.n_q,

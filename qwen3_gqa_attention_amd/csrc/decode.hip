@@ -24,10 +24,20 @@
 
 namespace q3 {
 
-constexpr int kDecodeChunk = 512;  // keys per workgroup
-constexpr int kDecodeUnroll = 4;   // keys per 16-lane group per iteration
+constexpr int kDecodeUnroll = 4;  // keys per 16-lane group per iteration
 
-int decode_chunk_keys() { return kDecodeChunk; }
+// Keys per workgroup: the largest of 2048, 1024, 512 that still launches at
+// least 2048 workgroups (8 per CU) for `span` keys per (sequence, KV head).
+// Longer chunks mean fewer workgroup start-ups and fewer partials to merge;
+// too few workgroups leave the last round's CUs with little in flight.
+// Measured on the 64-sequence decode step (1024..32768 keys): full caches
+// 0.760 / 0.752 / 0.736 ms at 512 / 1024 / 2048 keys (4096: 0.738); a
+// 4096-key window 0.192 / 0.189 / 0.195 ms.
+int decode_chunk_keys(int N, int n_kv, int64_t span) {
+  int c = 2048;
+  while (c > 512 && (int64_t)N * n_kv * ((span + c - 1) / c) < 2048) c >>= 1;
+  return c;
+}
 
 // Streaming 16-byte load: the cache is read once per step, so it is fetched
 // with the non-temporal hint and does not displace reused lines in L2 / MALL
@@ -69,21 +79,21 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
                                                           float* __restrict__ part_acc,
                                                           float* __restrict__ part_ml, int n_q,
                                                           int n_kv, KvAddr kv, int nchunk,
-                                                          int window) {
+                                                          int chunk, int window) {
   const int g = blockIdx.y, s = blockIdx.z;
   const int nkeys = positions[s] + 1;
   // Sliding window W (0: none): only the last W keys are visible, and the
   // grid spans only the chunks a window can overlap, counted from the one
   // holding the sequence's first visible key.
   const int klo = window > 0 ? max(0, nkeys - window) : 0;
-  const int c = klo / kDecodeChunk + blockIdx.x;
-  const int k0 = c * kDecodeChunk;
-  if (k0 >= nkeys || k0 + kDecodeChunk <= klo) return;
-  const int k1 = min(k0 + kDecodeChunk, nkeys);
+  const int c = klo / chunk + blockIdx.x;
+  const int k0 = c * chunk;
+  if (k0 >= nkeys || k0 + chunk <= klo) return;
+  const int k1 = min(k0 + chunk, nkeys);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, oct = lane & 15;
-  constexpr int SUB = kDecodeChunk / 4;
+  const int SUB = chunk / 4;
   const int wk0 = k0 + wave * SUB;
   const int wk1 = min(wk0 + SUB, k1);
 
@@ -325,15 +335,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
                                                              const float* __restrict__ part_ml,
                                                              const int32_t* __restrict__ positions,
                                                              T* __restrict__ Out, int n_q, int n_kv,
-                                                             int nchunk, int window) {
+                                                             int nchunk, int chunk,
+                                                             int window) {
   constexpr int U = 8, NW = 4;
   const int head = blockIdx.x, s = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n_rep = n_q / n_kv;
   const int g = head / n_rep, r = head % n_rep;
   const int nkeys = positions[s] + 1;
-  const int nc = (nkeys + kDecodeChunk - 1) / kDecodeChunk;
-  const int c_lo = window > 0 ? max(0, nkeys - window) / kDecodeChunk : 0;  // first chunk written
+  const int nc = (nkeys + chunk - 1) / chunk;
+  const int c_lo = window > 0 ? max(0, nkeys - window) / chunk : 0;  // first chunk written
   const size_t base = (size_t)(s * n_kv + g) * nchunk;
   float M = -INFINITY, lt = 0.f, a0 = 0.f, a1 = 0.f;
   for (int c0 = c_lo + wave; c0 < nc; c0 += NW * U) {
@@ -402,7 +413,8 @@ static void launch_decode_nrep(const T* Q, const T* Kc, const T* Vc, const int32
   // window of W keys the ceil(W / chunk) + 1 chunks it can overlap
   const int gx = ws.nchunk;
   hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(gx, n_kv, N), dim3(256), 0, s, Q,
-                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, kv, ws.nchunk, window);
+                     Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, kv, ws.nchunk,
+                     ws.chunk, window);
 }
 
 template <typename T>
@@ -424,7 +436,7 @@ hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(n_q, N), dim3(256), 0, s, ws.part_acc,
-                     ws.part_ml, positions, Out, n_q, n_kv, ws.nchunk, window);
+                     ws.part_ml, positions, Out, n_q, n_kv, ws.nchunk, ws.chunk, window);
   return hipGetLastError();
 }
 

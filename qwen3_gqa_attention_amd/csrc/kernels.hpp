@@ -140,9 +140,9 @@ struct DecodeScratch {
   float* part_ml;   // [N, n_kv, nchunk, n_rep, 2]
   int nchunk;       // chunks launched per (sequence, KV head): all of the cache, or with a
                     // window the ceil(W / chunk) + 1 it can overlap (slot = index in that span)
-  int chunk;
+  int chunk;        // keys per chunk (decode_chunk_keys)
 };
-int decode_chunk_keys();
+int decode_chunk_keys(int N, int n_kv, int64_t span);  // keys per chunk for `span` keys
 bool decode_nrep_supported(int n_rep);
 template <typename T>
 hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,
