@@ -549,7 +549,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="run only the prefill step and the full-attention decode (the two "
                          "roofline kernels), e.g. under a profiler")
-    ap.add_argument("--only", choices=["4b", "wide-gqa", "chunk", "decode", "decode-window"],
+    ap.add_argument("--only", choices=["4b", "wide-gqa", "chunk", "decode", "decode-window",
+                                       "decode-paged"],
                     help="time one secondary workload alone and print its own JSON line "
                          "(for profiling it by itself; not the headline line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -578,6 +579,8 @@ def main():
     if args.only:
         if args.only == "chunk":
             r = bench_chunk(args)
+        elif args.only == "decode-paged":
+            r = bench_decode_paged(args)
         elif args.only.startswith("decode"):
             W = 4096 if args.only == "decode-window" else 0
             dd = bench_decode(args, window=W)

@@ -87,8 +87,10 @@ bool ws_layout_prefill(const qwen3_attn_desc* d, int32_t B, int32_t n_tok, int32
   return true;
 }
 
+// Decode: `paged` picks the chunk length of a paged cache (cap = its
+// max_blocks * block_size slots per sequence).
 bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, int64_t cap,
-               WsLayout* L) {
+               WsLayout* L, bool paged = false) {
   if (check_desc(d) != QWEN3_ATTN_OK) return false;
   if (n <= 0 || T <= 0) return false;
   const size_t es = elem_size(d->dtype);
@@ -100,7 +102,7 @@ bool ws_layout(const qwen3_attn_desc* d, int is_decode, int32_t n, int32_t T, in
   if (T != 1 || cap <= 0 || cap > INT_MAX) return false;
   // keys per chunk, from the most keys one (sequence, KV head) can see
   const int64_t span = d->sliding_window > 0 ? std::min<int64_t>(cap, d->sliding_window) : cap;
-  const int chunk = q3::decode_chunk_keys(n, d->n_kv, span);
+  const int chunk = q3::decode_chunk_keys(n, d->n_kv, span, paged);
   // partial slots per (sequence, KV head): every chunk of the cache, or with a
   // sliding window only the chunks one window can overlap
   int64_t nchunk = (cap + chunk - 1) / chunk;
@@ -358,7 +360,11 @@ size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
                                  int32_t T, int64_t cache_cap) {
   WsLayout L;
   if (!ws_layout(desc, is_decode ? 1 : 0, B_or_N, T, cache_cap, &L)) return 0;
-  return L.total;
+  if (!is_decode) return L.total;
+  // one size for either kind of cache (a paged one may take shorter chunks)
+  WsLayout P;
+  if (!ws_layout(desc, 1, B_or_N, T, cache_cap, &P, true)) return 0;
+  return L.total > P.total ? L.total : P.total;
 }
 
 size_t qwen3_attn_workspace_size_varlen(const qwen3_attn_desc* desc, int32_t B,
@@ -418,7 +424,8 @@ qwen3_attn_status decode_entry(qwen3_attn_t* h, const void* hidden, const int32_
   if (N > 65535 || cache_cap > INT_MAX) return QWEN3_ATTN_EUNSUPPORTED;
   if (!q3::decode_nrep_supported(h->desc.n_q / h->desc.n_kv)) return QWEN3_ATTN_EUNSUPPORTED;
   WsLayout L;
-  if (!ws_layout(&h->desc, 1, N, 1, cache_cap, &L)) return QWEN3_ATTN_EUNSUPPORTED;
+  if (!ws_layout(&h->desc, 1, N, 1, cache_cap, &L, paged != nullptr))
+    return QWEN3_ATTN_EUNSUPPORTED;
   if (!workspace || workspace_bytes < L.total) return QWEN3_ATTN_EWORKSPACE;
   qwen3_attn_status st = check_handle_device(h);
   if (st != QWEN3_ATTN_OK) return st;

@@ -26,14 +26,18 @@ namespace q3 {
 
 constexpr int kDecodeUnroll = 4;  // keys per 16-lane group per iteration
 
-// Keys per workgroup: the largest of 2048, 1024, 512 that still launches at
-// least 2048 workgroups (8 per CU) for `span` keys per (sequence, KV head).
+// Keys per workgroup for a contiguous cache: the largest of 2048, 1024, 512
+// that still launches at least 2048 workgroups (8 per CU) for `span` keys
+// per (sequence, KV head).
 // Longer chunks mean fewer workgroup start-ups and fewer partials to merge;
 // too few workgroups leave the last round's CUs with little in flight.
 // Measured on the 64-sequence decode step (1024..32768 keys): full caches
 // 0.760 / 0.752 / 0.736 ms at 512 / 1024 / 2048 keys (4096: 0.738); a
 // 4096-key window 0.192 / 0.189 / 0.195 ms.
-int decode_chunk_keys(int N, int n_kv, int64_t span) {
+int decode_chunk_keys(int N, int n_kv, int64_t span, bool paged) {
+  // A paged cache (a block-table lookup every 16 keys) measured best at 512
+  // keys: 0.78 against 0.89 ms at 2048 on the same step.
+  if (paged) return 512;
   int c = 2048;
   while (c > 512 && (int64_t)N * n_kv * ((span + c - 1) / c) < 2048) c >>= 1;
   return c;
@@ -91,7 +95,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
   if (k0 >= nkeys || k0 + chunk <= klo) return;
   const int k1 = min(k0 + chunk, nkeys);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (read from the first lane), so that the key range and the
+  // cache-block lookups below stay in scalar registers: a block-table entry
+  // then comes through the scalar cache instead of a vector load (whose
+  // result, moved to a scalar register, would first wait for every row load
+  // in flight)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4, oct = lane & 15;
   const int SUB = chunk / 4;
   const int wk0 = k0 + wave * SUB;
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
   };
   // Keys outer, heads inner: each row is widened to fp32 once and used by
   // all n_rep heads at once (per head, the compiler keeps every widened row
-  // live across the heads: 2 heads took 190 VGPRs instead of 139).
+  // live across the heads).
   auto consume = [&](Rows& b) {
     if constexpr (NREP > 8) {
       consume_per_head(b);
@@ -243,35 +253,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     }
   };
   // Iterations stay on the 4U-key grid; keys below klo in the first one are
-  // masked.  For 2..8 heads per KV head, two row buffers: the next
-  // iteration's loads are issued before the current one is consumed, so each
-  // wave keeps two iterations in flight (bf16, 2 heads: 139 VGPRs, three
-  // waves per SIMD, against 126 and four single-buffered: 48 against 32 KB
-  // in flight per SIMD).  One head already has eight waves per SIMD, and 16
-  // heads would spill.
-  constexpr bool kTwoBuffers = NREP >= 2 && NREP <= 8;
-  int kb = max(wk0, klo & ~(4 * U - 1));
-  if constexpr (!kTwoBuffers) {
-    for (; kb < wk1; kb += 4 * U) {
-      Rows b;
-      load(b, kb);
-      consume(b);
-    }
-  } else if (kb < wk1) {
-    Rows ba, bb;
-    load(ba, kb);
-    while (true) {
-      const bool more_b = kb + 4 * U < wk1;
-      if (more_b) load(bb, kb + 4 * U);
-      consume(ba);
-      if (!more_b) break;
-      kb += 4 * U;
-      const bool more_a = kb + 4 * U < wk1;
-      if (more_a) load(ba, kb + 4 * U);
-      consume(bb);
-      if (!more_a) break;
-      kb += 4 * U;
-    }
+  // masked.  One row buffer: the loop streams at 7.0-7.5 TB/s in steady
+  // state already, and a second buffer (the next iteration's rows loaded
+  // before the current ones are consumed) measured slower.
+  for (int kb = max(wk0, klo & ~(4 * U - 1)); kb < wk1; kb += 4 * U) {
+    Rows b;
+    load(b, kb);
+    consume(b);
   }
 
   // Merge the four 16-lane groups of the wave (lanes oct, oct+16, +32, +48).

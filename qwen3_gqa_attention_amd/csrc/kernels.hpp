@@ -142,7 +142,8 @@ struct DecodeScratch {
                     // window the ceil(W / chunk) + 1 it can overlap (slot = index in that span)
   int chunk;        // keys per chunk (decode_chunk_keys)
 };
-int decode_chunk_keys(int N, int n_kv, int64_t span);  // keys per chunk for `span` keys
+// keys per chunk for `span` keys per (sequence, KV head), contiguous or paged cache
+int decode_chunk_keys(int N, int n_kv, int64_t span, bool paged);
 bool decode_nrep_supported(int n_rep);
 template <typename T>
 hipError_t launch_decode_attn(const T* Q, const T* Kc, const T* Vc, const int32_t* positions,

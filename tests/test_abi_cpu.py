@@ -88,11 +88,12 @@ def test_workspace_size_prefill_and_decode(built_lib):
     part = 8 * 128 * 16 * (128 + 2) * 4
     assert (q3.qwen3_attn_workspace_size(d32, 0, 1, 128, 0)
             == 2 * align(128 * 2048 * 4) + align(part))
-    # decode: q and merged output, then per-chunk partials; 64 sequences x 8 KV
-    # heads over 32832 slots take 2048-key chunks (17 per sequence and head:
-    # at least 2048 workgroups)
+    # decode: q and merged output, then per-chunk partials.  The size covers a
+    # contiguous cache (64 sequences x 8 KV heads over 32832 slots: 2048-key
+    # chunks) and a paged one of as many slots (512-key chunks), so the paged
+    # one's 65 chunks per sequence and head are reserved
     cap, N = 32832, 64
-    nchunk = -(-cap // 2048)
+    nchunk = -(-cap // 512)
     slots = N * 8 * nchunk * 2
     # bf16 64-row projections: the unsplit fp32 q/k/v product (64 x 4096) that
     # the finishing kernel normalises (o_proj needs none)
@@ -107,10 +108,11 @@ def test_workspace_size_prefill_and_decode(built_lib):
     want = 2 * align(N * 2048 * 4) + align(slots * 128 * 4) + align(slots * 2 * 4) + align(part)
     assert q3.qwen3_attn_workspace_size(d32, 1, N, 1, cap) == want
     # a sliding window of W keys: partial slots for the ceil(W / chunk) + 1
-    # chunks it can overlap; a 4096-key window takes 1024-key chunks (64 x 8 x
-    # 4 = 2048 workgroups)
+    # chunks it can overlap; a 4096-key window takes 1024-key chunks over a
+    # contiguous cache (64 x 8 x 4 = 2048 workgroups), 512-key ones over a
+    # paged one (9 slots: reserved)
     dw = desc(sliding_window=4096)
-    slots_w = N * 8 * 5 * 2
+    slots_w = N * 8 * 9 * 2
     want = (2 * align(N * 2048 * 2) + align(slots_w * 128 * 4) + align(slots_w * 2 * 4)
             + align(64 * 4096 * 4))
     assert q3.qwen3_attn_workspace_size(dw, 1, N, 1, cap) == want

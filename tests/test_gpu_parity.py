@@ -652,10 +652,15 @@ def test_prefill_paged_parity(dtype, bs, T, past):
     blk.close()
 
 
-def test_decode_paged_full_size_equals_contiguous():
+def test_decode_paged_full_size_matches_contiguous():
     # 64 sequences of 1024..32768 cached tokens in 64-token blocks laid out in
-    # a shuffled pool: the paged call equals the contiguous one bit for bit
-    # (the contiguous path is checked against the oracle at this size above).
+    # a shuffled pool, against the contiguous call on the same caches (that
+    # path is checked against the oracle at this size above).  The two split
+    # the keys into chunks of different lengths (512 over a paged pool, 2048
+    # over a contiguous cache of this size), so their log-sum-exp merges add
+    # the same terms in a different order: Y agrees to the bf16 bar, and the
+    # new token's K/V rows, written by the same projection kernel, are
+    # identical.
     import torch
     w = WORKLOADS[5]
     say(f"paged decode full size: {w.name}")
@@ -681,7 +686,15 @@ def test_decode_paged_full_size_equals_contiguous():
     y_p = blk.decode_paged(x, pos, table, kp, vp)
     y_c = blk.decode(x, pos, kc, vc)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(y_p), host(y_c))
+    assert np.all(np.isfinite(host(y_p)))
+    assert_close(host(y_p), host(y_c), w.dtype, "paged vs contiguous Y")
+    seq = torch.arange(w.B, device="cuda")
+    posl = pos.long()
+    phys = table[seq, posl // bs].long()
+    for pool, cache, what in ((kp, kc, "k"), (vp, vc, "v")):
+        new_p = pool[phys, :, posl % bs]             # [B, n_kv, 128]
+        new_c = cache[seq, :, posl]
+        assert torch.equal(new_p, new_c), f"new {what} rows differ"
     blk.close()
     del kc, vc, kp, vp
     torch.cuda.empty_cache()

@@ -215,6 +215,7 @@ def test_window_decode_paged_parity():
     torch.cuda.synchronize()
     ref = oracle.decode(inp["X"], *weights(inp), lens, kc, vc, **okw(w, W))
     assert_close(host(y_p), ref["Y"], w.dtype, "windowed paged decode Y")
+    # at this size both calls take 512-key chunks, so they match bit for bit
     np.testing.assert_array_equal(host(y_p), host(y_c))
     blk.close()
 
