@@ -400,7 +400,17 @@ static void launch_decode_nrep(const T* Q, const T* Kc, const T* Vc, const int32
   // ws.nchunk chunks per (sequence, KV head): all of the cache, or with a
   // window of W keys the ceil(W / chunk) + 1 chunks it can overlap
   const int gx = ws.nchunk;
-  hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(gx, n_kv, N), dim3(256), 0, s, Q,
+  // Residency: a short launch (at most 16 workgroups per CU in all) streams
+  // faster with 2 resident per CU than with the 5 its registers allow (64
+  // sequences, a 4096-key window: 0.188 against 0.194 ms; 3 per CU 0.189);
+  // for long ones (full caches, paged pools) a cap measured within noise
+  // either way (0.731-0.740 against 0.732-0.737 ms), so they are left alone.
+  // The cap is dynamic LDS the kernel does not use, on top of its own merge
+  // buffers (160 KB per CU).
+  constexpr int kStaticLds = (4 * NREP * 2 + 4 * NREP * kHeadDim) * (int)sizeof(float);
+  const int64_t per_cu = (int64_t)gx * n_kv * N / 256;
+  const int pad = per_cu <= 16 ? 160 * 1024 / 2 - kStaticLds - 256 : 0;
+  hipLaunchKernelGGL((decode_attn_kernel<T, NREP>), dim3(gx, n_kv, N), dim3(256), pad, s, Q,
                      Kc, Vc, positions, ws.part_acc, ws.part_ml, n_q, n_kv, kv, ws.nchunk,
                      ws.chunk, window);
 }
