@@ -330,27 +330,47 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n_rep = n_q / n_kv;
   const int g = head / n_rep, r = head % n_rep;
+  const size_t base = (size_t)(s * n_kv + g) * nchunk;
+  // Slots are numbered from the first chunk written (j = c - c_lo), so the
+  // first batch is loaded before the sequence length arrives (every slot
+  // below nchunk is allocated; the unwritten ones are masked after).
+  float M = -INFINITY, lt = 0.f, a0 = 0.f, a1 = 0.f;
+  float mv[U], lv[U];
+  f32x2_v av[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int jj = min(wave + NW * u, nchunk - 1);
+    const size_t sl = (base + jj) * n_rep + r;
+    mv[u] = part_ml[sl * 2];
+    lv[u] = part_ml[sl * 2 + 1];
+    av[u] = *reinterpret_cast<const f32x2_v*>(part_acc + sl * kHeadDim + 2 * lane);
+  }
   const int nkeys = positions[s] + 1;
   const int nc = (nkeys + chunk - 1) / chunk;
   const int c_lo = window > 0 ? max(0, nkeys - window) / chunk : 0;  // first chunk written
-  const size_t base = (size_t)(s * n_kv + g) * nchunk;
-  float M = -INFINITY, lt = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int c0 = c_lo + wave; c0 < nc; c0 += NW * U) {
-    float mv[U], lv[U];
-    f32x2_v av[U];
+  const int nw = nc - c_lo;                                          // slots written
+  for (int j0 = wave; j0 < nw; j0 += NW * U) {
+    if (j0 > wave) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int jj = min(j0 + NW * u, nchunk - 1);
+        const size_t sl = (base + jj) * n_rep + r;
+        mv[u] = part_ml[sl * 2];
+        lv[u] = part_ml[sl * 2 + 1];
+        av[u] = *reinterpret_cast<const f32x2_v*>(part_acc + sl * kHeadDim + 2 * lane);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = c0 + NW * u;
-      const size_t sl = (base + (c - c_lo)) * n_rep + r;
-      const bool ok = c < nc;
-      mv[u] = ok ? part_ml[sl * 2] : -INFINITY;
-      lv[u] = ok ? part_ml[sl * 2 + 1] : 0.f;
-      av[u] = ok ? *reinterpret_cast<const f32x2_v*>(part_acc + sl * kHeadDim + 2 * lane)
-                 : f32x2_v{0.f, 0.f};
+      if (j0 + NW * u >= nw) {
+        mv[u] = -INFINITY;
+        lv[u] = 0.f;
+        av[u] = f32x2_v{0.f, 0.f};
+      }
     }
     float mx = M;
 #pragma unroll
-    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);  // finite: chunk c0 < nc is written
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);  // finite: slot j0 < nw is written
     const float sc = exp2f(M - mx);   // 0 on the first pass (M = -inf)
     a0 *= sc;
     a1 *= sc;
@@ -365,7 +385,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     M = mx;
   }
   // Waves without a chunk keep M = -inf and contribute nothing; wave 0
-  // always has chunk c_lo.
+  // always has slot 0.
   __shared__ float sm_ml[NW][2];
   __shared__ float sm_a[NW][kHeadDim];
   if (lane == 0) {

@@ -642,7 +642,10 @@ static hipError_t launch_skinny(const bf16_t* A, const bf16_t* W, int M, int N, 
 // columns) and 16 rows, then QK-Norm, RoPE and the stores, as the GEMM
 // epilogue does.  256 threads: row = 16 * blockIdx.y + tid / 16 (one DPP row
 // of 16 lanes per token), columns 8 * (tid % 16) .. + 7.  cos/sin are
-// evaluated here from positions and omega / (2 pi) (hi + lo floats).
+// evaluated here from positions and omega / (2 pi) (hi + lo floats).  Every
+// load that does not depend on another (the first K slice, the row's
+// position, the gain, the RoPE constants) is issued before any is used, so
+// the kernel waits for memory once.
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
                                                          int M, int N, int K, QkvEpilogue qe) {
@@ -652,25 +655,39 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
   const int kind = head < qe.n_q ? 0 : (head < qe.n_q + qe.n_kv ? 1 : 2);
   const bool ok = row < M;
   const int r = ok ? row : 0;
-  float v[8];
+  const float* p0 = part + (size_t)r * N + head * kHeadDim + j * 8;
+  f32x4_v x0 = *reinterpret_cast<const f32x4_v*>(p0);
+  f32x4_v x1 = *reinterpret_cast<const f32x4_v*>(p0 + 4);
+  const int pos = qe.positions[r];
+  const T* gp = reinterpret_cast<const T*>(kind == 0 ? qe.gq : qe.gk) + j * 8;
+  T g8[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = 0.f;
-  for (int k0 = 0; k0 < ks; k0 += 4) {  // four slices' loads in flight at once
+  for (int e = 0; e < 8; ++e) g8[e] = gp[e];
+  const float* rp = qe.rope_rev + (j & 7) * 8;
+  const f32x4_v rh0 = *reinterpret_cast<const f32x4_v*>(rp);
+  const f32x4_v rh1 = *reinterpret_cast<const f32x4_v*>(rp + 4);
+  const f32x4_v rl0 = *reinterpret_cast<const f32x4_v*>(rp + 64);
+  const f32x4_v rl1 = *reinterpret_cast<const f32x4_v*>(rp + 68);
+  for (int k0 = 1; k0 < ks; k0 += 4) {  // the other slices, four loads in flight at once
     f32x4_v x[4][2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float* p = part + ((size_t)(k0 + u) * M + r) * N + head * kHeadDim + j * 8;
+      const float* p = p0 + (size_t)(k0 + u) * M * N;
       const bool in = k0 + u < ks;
       x[u][0] = in ? *reinterpret_cast<const f32x4_v*>(p) : f32x4_v{0.f, 0.f, 0.f, 0.f};
       x[u][1] = in ? *reinterpret_cast<const f32x4_v*>(p + 4) : f32x4_v{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u) {
+      x0 += x[u][0];
+      x1 += x[u][1];
+    }
+  }
+  float v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] += x[u][0][e];
-        v[4 + e] += x[u][1][e];
-      }
+  for (int e = 0; e < 4; ++e) {
+    v[e] = x0[e];
+    v[4 + e] = x1[e];
   }
   if (qe.in_norm_x) {
     // Input RMSNorm (gain folded into the weights): 1/rms of the row of x,
@@ -695,17 +712,14 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
     for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
     ss = row16_sum(ss);
     const float rs = rsqrtf(ss * (1.f / 128.f) + qe.eps);
-    const T* g = reinterpret_cast<const T*>(kind == 0 ? qe.gq : qe.gk);
     const float gs = rs * (kind == 0 ? qe.q_scale : 1.f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= gs * to_f32<T>(g[j * 8 + e]);
+    for (int e = 0; e < 8; ++e) v[e] *= gs * to_f32<T>(g8[e]);
     // RoPE: column c pairs with c + 64, i.e. thread j with j ^ 8 (DPP row_ror:8).
-    const int pos = qe.positions[r];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int f = (j & 7) * 8 + e;
       float sn, cn;
-      rope_sincos(pos, qe.rope_rev[f], qe.rope_rev[64 + f], &sn, &cn);
+      rope_sincos(pos, e < 4 ? rh0[e] : rh1[e - 4], e < 4 ? rl0[e] : rl1[e - 4], &sn, &cn);
       const float other = dpp_move<0x128>(v[e]);
       v[e] = (j < 8) ? v[e] * cn - other * sn : v[e] * cn + other * sn;
     }
