@@ -719,24 +719,38 @@ __global__ __launch_bounds__(KSPLIT * 256, 2) void flash_prefill_kernel(const T*
 
 // Merge the nsplit partial results of each (token, query head): one online
 // log-sum-exp pass over the parts, then O / l rounded to T.  32 threads per
-// (token, head), 4 dims each (16-byte loads); 8 pairs per workgroup.
-template <typename T>
+// (token, head), 4 dims each (16-byte loads); 8 pairs per workgroup.  The
+// parts are all loaded before the pass (NS >= nsplit slots: 2, 4 or 8), so
+// the kernel waits for memory once.
+constexpr int kMaxSplits = 8;
+template <typename T, int NS>
 __global__ __launch_bounds__(256) void flash_combine_kernel(const float* __restrict__ part,
                                                             int nsplit, int pairs,
                                                             T* __restrict__ Out) {
   const int pair = blockIdx.x * 8 + (threadIdx.x >> 5), d = (threadIdx.x & 31) * 4;
   if (pair >= pairs) return;
   const float* pml = part + (size_t)nsplit * pairs * kHeadDim;
+  f32x2_v ml[NS];
+  f32x4_v ops[NS];
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) {
+    const size_t row = (size_t)min(sp, nsplit - 1) * pairs + pair;
+    ml[sp] = *reinterpret_cast<const f32x2_v*>(pml + row * 2);
+    ops[sp] = *reinterpret_cast<const f32x4_v*>(part + row * kHeadDim + d);
+  }
+  // Branch-free, so that the loads above stay ahead of the pass: a part
+  // past nsplit, or with no key visible to the row, enters with weights
+  // (1, 0) and leaves M, l and O as they are.
   float M = -INFINITY, l = 0.f;
   f32x4_v o = f32x4_v{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const size_t row = (size_t)sp * pairs + pair;
-    const float m = pml[row * 2], lp = pml[row * 2 + 1];
-    const f32x4_v op = *reinterpret_cast<const f32x4_v*>(part + row * kHeadDim + d);
-    if (m == -INFINITY) continue;  // no key of this part is visible to the row
-    const float mn = fmaxf(M, m);
-    const float a = __builtin_amdgcn_exp2f(M - mn);  // 0 while M is -inf
-    const float w = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) {
+    const bool use = sp < nsplit && ml[sp][0] != -INFINITY;
+    const float m = ml[sp][0], lp = ml[sp][1];
+    const f32x4_v op = ops[sp];
+    const float mn = use ? fmaxf(M, m) : M;
+    const float a = use ? __builtin_amdgcn_exp2f(M - mn) : 1.f;  // 0 while M is -inf
+    const float w = use ? __builtin_amdgcn_exp2f(m - mn) : 0.f;
     l = l * a + lp * w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = o[e] * a + op[e] * w;
@@ -757,7 +771,7 @@ int flash_splits(int B, int T_len, int n_q, int n_kv) {
   const int wgs = flash_query_wgs(B, T_len, n_q, n_kv);
   if (wgs >= 256) return 1;
   const int sp = 256 / wgs;
-  return sp < 2 ? 2 : (sp > 8 ? 8 : sp);
+  return sp < 2 ? 2 : (sp > kMaxSplits ? kMaxSplits : sp);
 }
 size_t flash_partial_floats(int B, int T_len, int n_q, int n_kv, int n_tok) {
   const int sp = flash_splits(B, T_len, n_q, n_kv);
@@ -808,8 +822,16 @@ hipError_t launch_flash_prefill(const T* Q, const T* Kc, const T* Vc, T* Out, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int pairs = n_tok * n_q;
-    hipLaunchKernelGGL(flash_combine_kernel<T>, dim3((pairs + 7) / 8), dim3(256), 0, s, part,
-                       nsplit, pairs, Out);
+    const dim3 grid((pairs + 7) / 8);
+    if (nsplit <= 2)
+      hipLaunchKernelGGL((flash_combine_kernel<T, 2>), grid, dim3(256), 0, s, part, nsplit, pairs,
+                         Out);
+    else if (nsplit <= 4)
+      hipLaunchKernelGGL((flash_combine_kernel<T, 4>), grid, dim3(256), 0, s, part, nsplit, pairs,
+                         Out);
+    else
+      hipLaunchKernelGGL((flash_combine_kernel<T, kMaxSplits>), grid, dim3(256), 0, s, part,
+                         nsplit, pairs, Out);
   }
   return hipGetLastError();
 }
