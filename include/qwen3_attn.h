@@ -130,7 +130,9 @@ qwen3_attn_status qwen3_attn_create_with_input_norm(const qwen3_attn_desc* desc,
  * Pure host computation, no HIP call.
  *   is_decode = 0: prefill of B_or_N sequences of T tokens (cache_cap unused);
  *   is_decode = 1: decode of B_or_N sequences (T must be 1), caches of
- *                  cache_cap slots. */
+ *                  cache_cap slots -- contiguous, or paged with cache_cap =
+ *                  max_blocks * block_size: the size serves either (a
+ *                  contiguous cache may need less). */
 size_t qwen3_attn_workspace_size(const qwen3_attn_desc* desc, int32_t is_decode,
                                  int32_t B_or_N, int32_t T, int64_t cache_cap);
 
@@ -305,9 +307,10 @@ qwen3_attn_status qwen3_attn_forward_decode(qwen3_attn_t* h, const void* hidden,
  * results, minus the workspace.  Its scratch memory is a static device array
  * of QWEN3_ATTN_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU,
  * held until the process ends; the call allocates and frees nothing.
- *   - A call whose qwen3_attn_workspace_size(desc, 1, N, 1, cache_cap) exceeds
- *     QWEN3_ATTN_NOALLOC_SCRATCH_BYTES returns EWORKSPACE and launches
- *     nothing (the 0.6B shape fits 64 sequences with caches of 32832 slots).
+ *   - A call that needs more than QWEN3_ATTN_NOALLOC_SCRATCH_BYTES of scratch
+ *     (at most qwen3_attn_workspace_size(desc, 1, N, 1, cache_cap)) returns
+ *     EWORKSPACE and launches nothing (the 0.6B shape fits 64 sequences with
+ *     caches of 32832 slots).
  *   - Every call on one GPU shares that GPU's array: calls that overlap on a
  *     GPU (several streams or host threads) race and give wrong results.
  *     Serialise them, or use qwen3_attn_forward_decode with a workspace each.

@@ -63,7 +63,7 @@ struct WsLayout {
   size_t q_off, a_off, acc_off, ml_off, part_off, total;
   int nchunk;
   int chunk;  // decode: keys per chunk
-  bool part;  // decode projections run split-K through the part region
+  bool part;  // decode (<= 64 rows): the projections' fp32 products go through the part region
 };
 
 // Prefill of B sequences with n_tok token rows in all, at most max_T each.

@@ -494,13 +494,14 @@ static hipError_t launch_gemm(const T* A, const T* B, int M, int N, int K, const
 }
 
 // ---------------------------------------------------------------------------
-// Decode-sized projections (M <= 64 rows): bound by reading the weights, so
-// the K dimension is split over the grid (many workgroups streaming weights
-// at once) into fp32 partials, which a second kernel sums.
+// Decode-sized projections (M <= 64 rows), bound by reading the weights.
+// bf16: the skinny kernel below (whole K per workgroup, split over its
+// waves).  fp32: the K dimension is split over the grid (many workgroups
+// streaming weights at once) into fp32 partials, which a second kernel sums.
 // ---------------------------------------------------------------------------
 constexpr int kSmallM = 64;
 
-// Number of K slices for a decode projection: the fewest (a power of two,
+// Number of K slices for an fp32 decode projection: the fewest (a power of two,
 // each slice a whole number of 128-byte k-tiles) that give at least 64
 // workgroups.  More slices spread the weight stream over more CUs but write
 // and re-read more fp32 partials: at 64 rows, 64 workgroups measured fastest
