@@ -151,6 +151,16 @@ def steps_for_duration(step_s):
     return max(MIN_TIMED_STEPS, int(math.ceil(MIN_TIMED_S / max(step_s, 1e-9))))
 
 
+def decode_timing(args, fn):
+    """Warm-up, then the timed step count of a decode workload: --decode-steps
+    if given, else by duration (as the prefill shapes)."""
+    import torch
+    for _ in range(max(args.warmup, 10)):
+        fn()
+    torch.cuda.synchronize()
+    return args.decode_steps if args.decode_steps > 0 else steps_for_duration(estimate_step_s(fn))
+
+
 def estimate_step_s(fn, n=5):
     """Mean time of n back-to-back calls (after the caller's warm-up)."""
     import torch
@@ -339,10 +349,7 @@ def bench_decode(args, window=0):
     pos = torch.from_numpy(L).cuda()
     out = torch.empty_like(x)
     ws = torch.empty(blk.workspace_size(True, w.B, 1, w.cap), dtype=torch.uint8, device="cuda")
-    for _ in range(max(args.warmup // 2, 2)):
-        blk.decode(x, pos, kc, vc, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    steps = args.decode_steps
+    steps = decode_timing(args, lambda: blk.decode(x, pos, kc, vc, out=out, workspace=ws))
     t0 = time.perf_counter()
     for _ in range(steps):
         blk.decode(x, pos, kc, vc, out=out, workspace=ws)
@@ -368,7 +375,8 @@ def bench_decode(args, window=0):
     del kc, vc
     torch.cuda.empty_cache()
     return dict(step_s=step_s, kv_read=kv_read, weights=weights, stage_ms=[m / max(ncalls, 1) for m in stage_ms],
-                attn_ms=attn_ms, attn_bytes=attn_bytes, N=w.B, mean_len=float(L.mean()), w=w)
+                attn_ms=attn_ms, attn_bytes=attn_bytes, N=w.B, mean_len=float(L.mean()), w=w,
+                steps=steps)
 
 
 def bench_decode_paged(args, bs=64):
@@ -409,10 +417,8 @@ def bench_decode_paged(args, bs=64):
     tab = torch.from_numpy(table).cuda()
     out = torch.empty_like(x)
     ws = torch.empty(blk.workspace_size(True, w.B, 1, mb * bs), dtype=torch.uint8, device="cuda")
-    for _ in range(max(args.warmup // 2, 2)):
-        blk.decode_paged(x, pos, tab, kp, vp, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    steps = args.decode_steps
+    steps = decode_timing(args, lambda: blk.decode_paged(x, pos, tab, kp, vp, out=out,
+                                                          workspace=ws))
     t0 = time.perf_counter()
     for _ in range(steps):
         blk.decode_paged(x, pos, tab, kp, vp, out=out, workspace=ws)
@@ -423,7 +429,7 @@ def bench_decode_paged(args, bs=64):
     torch.cuda.empty_cache()
     nbytes = float(np.sum(L.astype(np.int64))) * 2 * w.n_kv * 128 * 2 + \
         ((w.n_q + 2 * w.n_kv) * 128 * w.d * 2 + w.d * w.n_q * 128 * 2)
-    return {"workload": f"{w.name}-paged-bs{bs}", "block_size": bs, "blocks": nb,
+    return {"workload": f"{w.name}-paged-bs{bs}", "block_size": bs, "blocks": nb, "steps": steps,
             "ms_per_step": step_s * 1e3, "tokens_per_s": w.B / step_s,
             "GBps": nbytes / step_s / 1e9, "frac_hbm_peak": nbytes / step_s / PEAK_HBM_BYTES}
 
@@ -543,7 +549,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="timed steps of each decode workload (0: by duration, at least "
+                         f"{MIN_TIMED_S} s and {MIN_TIMED_STEPS} steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
@@ -586,7 +594,7 @@ def main():
             dd = bench_decode(args, window=W)
             nbytes = dd["kv_read"] + dd["weights"]
             r = {"workload": dd["w"].name + (f"-window{W}" if W else ""), "window": W,
-                 "steps": args.decode_steps, "ms_per_step": dd["step_s"] * 1e3,
+                 "steps": dd["steps"], "ms_per_step": dd["step_s"] * 1e3,
                  "GBps": nbytes / dd["step_s"] / 1e9,
                  "frac_hbm_peak": nbytes / dd["step_s"] / PEAK_HBM_BYTES,
                  "kernel_ms": dict(zip(q3.STAGES, dd["stage_ms"]))}
@@ -631,6 +639,7 @@ def main():
         log(f"bench: decode {dd['step_s'] * 1e3:.4f} ms/step, attention kernels {dd['attn_ms']:.4f} ms")
         dec = {
             "workload": dd["w"].name, "sequences": dd["N"], "mean_cache_len": dd["mean_len"],
+            "steps": dd["steps"],
             "ms_per_step": dd["step_s"] * 1e3, "tokens_per_s": dd["N"] / dd["step_s"],
             "bytes_per_step": dd["kv_read"] + dd["weights"],
             "GBps": (dd["kv_read"] + dd["weights"]) / dd["step_s"] / 1e9,
@@ -647,7 +656,7 @@ def main():
         log(f"bench: decode, the same 64 sequences in a sliding-window layer (W={W})")
         dw = bench_decode(args, window=W)
         nbytes = dw["kv_read"] + dw["weights"]
-        dec_window = {"workload": f"{dw['w'].name}-window{W}", "window": W,
+        dec_window = {"workload": f"{dw['w'].name}-window{W}", "window": W, "steps": dw["steps"],
                       "ms_per_step": dw["step_s"] * 1e3, "tokens_per_s": dw["N"] / dw["step_s"],
                       "bytes_per_step": nbytes, "GBps": nbytes / dw["step_s"] / 1e9,
                       "frac_hbm_peak": nbytes / dw["step_s"] / PEAK_HBM_BYTES,
