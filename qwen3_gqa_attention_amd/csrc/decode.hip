@@ -27,19 +27,20 @@ namespace q3 {
 constexpr int kDecodeUnroll = 4;  // keys per 16-lane group per iteration
 
 // Keys per workgroup for a contiguous cache: the largest of 2048, 1024, 512
-// that still launches at least 2048 workgroups (8 per CU) for `span` keys
+// that still launches at least 1024 workgroups (4 per CU) for `span` keys
 // per (sequence, KV head).
 // Longer chunks mean fewer workgroup start-ups and fewer partials to merge;
 // too few workgroups leave the last round's CUs with little in flight.
 // Measured on the 64-sequence decode step (1024..32768 keys): full caches
 // 0.760 / 0.752 / 0.736 ms at 512 / 1024 / 2048 keys (4096: 0.738); a
-// 4096-key window 0.192 / 0.189 / 0.195 ms.
+// 4096-key window, with the launch's residency capped at 2 workgroups per
+// CU (below), 0.193 / 0.186 / 0.182 ms (4096: 0.209).
 int decode_chunk_keys(int N, int n_kv, int64_t span, bool paged) {
   // A paged cache (a block-table lookup every 16 keys) measured best at 512
   // keys: 0.78 against 0.89 ms at 2048 on the same step.
   if (paged) return 512;
   int c = 2048;
-  while (c > 512 && (int64_t)N * n_kv * ((span + c - 1) / c) < 2048) c >>= 1;
+  while (c > 512 && (int64_t)N * n_kv * ((span + c - 1) / c) < 1024) c >>= 1;
   return c;
 }
 
@@ -422,7 +423,8 @@ static void launch_decode_nrep(const T* Q, const T* Kc, const T* Vc, const int32
   const int gx = ws.nchunk;
   // Residency: a short launch (at most 16 workgroups per CU in all) streams
   // faster with 2 resident per CU than with the 5 its registers allow (64
-  // sequences, a 4096-key window: 0.188 against 0.194 ms; 3 per CU 0.189);
+  // sequences, a 4096-key window in 1024-key chunks: 0.188 against 0.194
+  // ms; 3 per CU 0.189; 1 per CU 0.239);
   // for long ones (full caches, paged pools) a cap measured within noise
   // either way (0.731-0.740 against 0.732-0.737 ms), so they are left alone.
   // The cap is dynamic LDS the kernel does not use, on top of its own merge

@@ -108,9 +108,9 @@ def test_workspace_size_prefill_and_decode(built_lib):
     want = 2 * align(N * 2048 * 4) + align(slots * 128 * 4) + align(slots * 2 * 4) + align(part)
     assert q3.qwen3_attn_workspace_size(d32, 1, N, 1, cap) == want
     # a sliding window of W keys: partial slots for the ceil(W / chunk) + 1
-    # chunks it can overlap; a 4096-key window takes 1024-key chunks over a
-    # contiguous cache (64 x 8 x 4 = 2048 workgroups), 512-key ones over a
-    # paged one (9 slots: reserved)
+    # chunks it can overlap; a 4096-key window takes 2048-key chunks over a
+    # contiguous cache (64 x 8 x 2 = 1024 workgroups: 3 slots), 512-key ones
+    # over a paged one (9 slots: reserved)
     dw = desc(sliding_window=4096)
     slots_w = N * 8 * 9 * 2
     want = (2 * align(N * 2048 * 2) + align(slots_w * 128 * 4) + align(slots_w * 2 * 4)
