@@ -36,8 +36,9 @@ constexpr int kDecodeUnroll = 4;  // keys per 16-lane group per iteration
 // 4096-key window, with the launch's residency capped at 2 workgroups per
 // CU (below), 0.193 / 0.186 / 0.182 ms (4096: 0.209).
 int decode_chunk_keys(int N, int n_kv, int64_t span, bool paged) {
-  // A paged cache (a block-table lookup every 16 keys) measured best at 512
-  // keys: 0.78 against 0.89 ms at 2048 on the same step.
+  // A paged cache (64-key blocks scattered over the pool, one scalar
+  // block-table lookup every 16 keys) measured best at 512 keys on the same
+  // step: 0.773 against 0.841 / 0.862 ms at 1024 / 2048.
   if (paged) return 512;
   int c = 2048;
   while (c > 512 && (int64_t)N * n_kv * ((span + c - 1) / c) < 1024) c >>= 1;
