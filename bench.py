@@ -34,12 +34,21 @@ CSRC = os.path.join(ROOT, "qwen3_gqa_attention_amd", "csrc")
 COPY_BYTES = 512 << 20        # bytes read (and written) by one calibration copy
 PMC_KERNELS = {               # roofline entry -> kernel-name substrings summed per launch
     "prefill_attention": ["flash_prefill_kernel"],
+    # the headline shape's q/k/v (256x256 tiles) and o_proj (128x128, K groups)
+    # GEMMs: the flash kernel and the q/k/v GEMM do the same FLOPs, so either
+    # can be the dominant kernel of a run
+    "prefill_qkv": ["gemm_nt_kernel<unsigned short, 4, 2, 2, 4, true, false, 2, false, 1>"],
+    "prefill_oproj": ["gemm_nt_kernel<unsigned short, 2, 2, 2, 2, false, false, 2, false, 2>"],
     "decode_attention": ["decode_attn_kernel", "decode_combine_kernel"],
 }
 KERNEL_SOURCES = {            # roofline entry -> the sources its kernels are built from
     "prefill_attention": ["flash_prefill.hip", "device_common.hpp", "kernels.hpp"],
+    "prefill_qkv": ["gemm.hip", "device_common.hpp", "kernels.hpp"],
+    "prefill_oproj": ["gemm.hip", "device_common.hpp", "kernels.hpp"],
     "decode_attention": ["decode.hip", "device_common.hpp", "kernels.hpp"],
 }
+PREFILL_TRAFFIC_KEY = {"attention": "prefill_attention", "qkv_norm_rope_gemm": "prefill_qkv",
+                       "o_proj_gemm": "prefill_oproj"}
 
 
 def kernel_source_hash(key):
@@ -322,8 +331,29 @@ def bench_chunk(args, P=1536, T=512):
             "kernels": kernels}
 
 
-def bench_decode(args, window=0):
-    """The 64-sequence decode; window > 0 makes it a sliding-window layer."""
+def decode_caches():
+    """The 64-sequence decode workload's KV caches (N(0,1) entries, bf16)."""
+    import torch
+
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[5]
+    bf = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    kc = torch.empty((w.B, w.n_kv, w.cap, 128), dtype=bf, device="cuda")
+    vc = torch.empty_like(kc)
+    for s in range(w.B):   # drawn per sequence to bound the fp32 temporary
+        kc[s] = torch.randn((w.n_kv, w.cap, 128), generator=gen, device="cuda").to(bf)
+        vc[s] = torch.randn((w.n_kv, w.cap, 128), generator=gen, device="cuda").to(bf)
+    return kc, vc
+
+
+def bench_decode(args, window=0, caches=None):
+    """The 64-sequence decode; window > 0 makes it a sliding-window layer.
+    caches: (k, v) from decode_caches() to reuse (the full and the windowed
+    decode share one allocation, as a server keeps its cache), else drawn
+    here and freed at the end."""
     import numpy as np
     import torch
 
@@ -338,13 +368,8 @@ def bench_decode(args, window=0):
     blk = q3.Qwen3Attention(d(inp["Wq"]), d(inp["Wk"]), d(inp["Wv"]), d(inp["Wo"]), d(inp["gq"]),
                             d(inp["gk"]), n_q=w.n_q, n_kv=w.n_kv, eps=EPS, rope_theta=ROPE_THETA,
                             sliding_window=window)
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(w.seed)
-    kc = torch.empty((w.B, w.n_kv, w.cap, 128), dtype=bf, device="cuda")
-    vc = torch.empty_like(kc)
-    for s in range(w.B):   # N(0,1) cache entries, drawn per sequence to bound the fp32 temporary
-        kc[s] = torch.randn((w.n_kv, w.cap, 128), generator=gen, device="cuda").to(bf)
-        vc[s] = torch.randn((w.n_kv, w.cap, 128), generator=gen, device="cuda").to(bf)
+    own = caches is None
+    kc, vc = decode_caches() if own else caches
     x = d(inp["X"])
     pos = torch.from_numpy(L).cuda()
     out = torch.empty_like(x)
@@ -372,8 +397,9 @@ def bench_decode(args, window=0):
     weights = (w.n_q + 2 * w.n_kv) * 128 * w.d * 2 + w.d * w.n_q * 128 * 2
     attn_ms = stage_ms[1] / max(ncalls, 1)
     attn_bytes = kv_read + w.B * w.n_kv * 2 * 128 * 2 + 2 * w.B * w.n_q * 128 * 2
-    del kc, vc
-    torch.cuda.empty_cache()
+    if own:
+        del kc, vc
+        torch.cuda.empty_cache()
     return dict(step_s=step_s, kv_read=kv_read, weights=weights, stage_ms=[m / max(ncalls, 1) for m in stage_ms],
                 attn_ms=attn_ms, attn_bytes=attn_bytes, N=w.B, mean_len=float(L.mean()), w=w,
                 steps=steps)
@@ -633,9 +659,11 @@ def main():
     else:
         prep = prepare_prefill()
         prep_layer = prepare_prefill(layer=True)
+    dcache = None
     if not args.no_decode:
         log("bench: decode 64 sequences, caches 1024..32768")
-        dd = bench_decode(args)
+        dcache = decode_caches()
+        dd = bench_decode(args, caches=dcache)
         log(f"bench: decode {dd['step_s'] * 1e3:.4f} ms/step, attention kernels {dd['attn_ms']:.4f} ms")
         dec = {
             "workload": dd["w"].name, "sequences": dd["N"], "mean_cache_len": dd["mean_len"],
@@ -654,7 +682,7 @@ def main():
     if extras and not args.no_decode:
         W = 4096
         log(f"bench: decode, the same 64 sequences in a sliding-window layer (W={W})")
-        dw = bench_decode(args, window=W)
+        dw = bench_decode(args, window=W, caches=dcache)
         nbytes = dw["kv_read"] + dw["weights"]
         dec_window = {"workload": f"{dw['w'].name}-window{W}", "window": W, "steps": dw["steps"],
                       "ms_per_step": dw["step_s"] * 1e3, "tokens_per_s": dw["N"] / dw["step_s"],
@@ -667,6 +695,12 @@ def main():
         dec_paged = bench_decode_paged(args)
         log(f"bench: paged decode {dec_paged['ms_per_step']:.4f} ms/step, "
             f"{dec_paged['frac_hbm_peak'] * 100:.1f}% of HBM peak")
+    if dcache is not None:
+        # freed only now, so that no decode workload runs on memory just
+        # released by another (a freshly re-allocated 8.6 GB cache measured
+        # 3-5% slower than the first allocation)
+        del dcache
+        torch.cuda.empty_cache()
     if extras:
         log("bench: prefill per-call times, hot and with the caches flushed")
         cold = bench_prefill_cold(args)
@@ -729,7 +763,7 @@ def main():
                      "achieved": p["flops"][dom] / (dk["avg_ms"] / 1e3) / 1e12,
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": p["flops"][dom] / (dk["avg_ms"] / 1e3) / PEAK_BF16_FLOPS,
-                     "traffic": traffic.get("prefill_attention") if dom == "attention" else None},
+                     "traffic": traffic.get(PREFILL_TRAFFIC_KEY[dom])},
         "prefill_per_call": cold,
         "prefill_other_shapes": other,
         "layer_prefill": layer,
