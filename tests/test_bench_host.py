@@ -45,18 +45,22 @@ def test_traffic_summary_scales_by_the_copy_and_guards_sources(tmp_path, monkeyp
     copy_kib = bench.COPY_BYTES / 1024
     fetch = tmp_path / "f.csv"
     write = tmp_path / "w.csv"
+    qkv, oproj = bench.PMC_KERNELS["prefill_qkv"], bench.PMC_KERNELS["prefill_oproj"]
     # the copy reads COPY_BYTES and FETCH_SIZE reports half of it: scale 2
     write_counter_csv(fetch, "FETCH_SIZE", [
         ("at::native::neg_kernel", copy_kib / 2), ("q3::flash_prefill_kernel<...>", 1000),
         ("q3::flash_prefill_kernel<...>", 1200), ("q3::decode_attn_kernel<...>", 300),
-        ("q3::decode_combine_kernel<...>", 20)])
+        ("q3::decode_combine_kernel<...>", 20)] + [(f"void q3::{s}(...)", 700)
+                                                   for s in qkv + oproj])
     write_counter_csv(write, "WRITE_SIZE", [
         ("at::native::neg_kernel", copy_kib), ("q3::flash_prefill_kernel<...>", 500),
-        ("q3::decode_attn_kernel<...>", 40), ("q3::decode_combine_kernel<...>", 4)])
+        ("q3::decode_attn_kernel<...>", 40), ("q3::decode_combine_kernel<...>", 4)]
+        + [(f"void q3::{s}(...)", 300) for s in qkv + oproj])
     bench.summarize_pmc(str(fetch), str(write), ["cmd one", "cmd two"])
     got = bench.load_traffic()
     assert got["prefill_attention"] == pytest.approx((1100 * 2 + 500) * 1024)
     assert got["decode_attention"] == pytest.approx(((300 + 20) * 2 + 40 + 4) * 1024)
+    assert got["prefill_qkv"] == pytest.approx((700 * 2 + 300) * 1024)
     text = open(bench.TRAFFIC_FILE).read()
     assert "cmd one" in text and "cmd two" in text
     # a record taken from other kernel sources is not used
@@ -64,7 +68,7 @@ def test_traffic_summary_scales_by_the_copy_and_guards_sources(tmp_path, monkeyp
     rec["source_hash"]["prefill_attention"] = "0" * 16
     with open(bench.TRAFFIC_FILE, "w") as f:
         f.write("TRAFFIC_JSON " + json.dumps(rec) + "\n")
-    assert set(bench.load_traffic()) == {"decode_attention"}
+    assert set(bench.load_traffic()) == {"decode_attention", "prefill_qkv", "prefill_oproj"}
 
 
 def test_traffic_summary_needs_the_copy_kernel(tmp_path, monkeypatch):
