@@ -123,10 +123,15 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
   constexpr int STAGE = (BM + BN) * BK;  // elements per LDS stage
   // epilogue staging (bf16 only; fp32 results are stored from registers)
   constexpr int STAGED = sizeof(T) == 2 ? (NT / 64) * (32 * MI) * (32 * NI + 8) : 0;
-  // KG > 1: the accumulators (and NORM sums of squares) of groups 1 .. KG-1,
-  // fp32, as [group - 1][wave][register][lane]
-  constexpr int MERGE1 = (NT / 64) * (MI * NI * 16 + MI) * 64;  // floats per group
-  constexpr int MERGE = KG > 1 ? (KG - 1) * MERGE1 * 4 / (int)sizeof(T) : 0;
+  // KG > 1: every group's accumulators (and NORM sums of squares), fp32, as
+  // [group][wave][lane][MROW] -- each lane's values contiguous, the row
+  // length padded to 4 mod 32 floats so that the 16-byte accesses of
+  // consecutive lanes fall on distinct banks.
+  constexpr int MVALS = MI * NI * 16 + MI;
+  constexpr int MROW = MVALS + ((4 - MVALS) % 32 + 32) % 32;
+  static_assert(MROW >= MVALS && MROW % 32 == 4, "merge row");
+  constexpr int MERGE1 = (NT / 64) * 64 * MROW;  // floats per group
+  constexpr int MERGE = KG > 1 ? KG * MERGE1 * 4 / (int)sizeof(T) : 0;
   constexpr int SMEM1 = KG * NSTAGE * STAGE > STAGED ? KG * NSTAGE * STAGE : STAGED;
   constexpr int SMEM = SMEM1 > MERGE ? SMEM1 : MERGE;
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 LDS stages");
@@ -271,37 +276,49 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
     }
   }
   lds_barrier();  // the epilogue reuses the LDS of the last tiles
+  // With K groups every group finishes a share of the tile: group kg sums
+  // elements kg*IE .. kg*IE + IE-1 of each accumulator block over the groups
+  // (in group order) and runs the epilogue on them -- rows rofs .. rofs +
+  // 32/KG - 1 of every 32-row block -- so all the waves share the epilogue.
+  constexpr int IE = KG > 1 ? 16 / KG : 16;  // accumulator elements finished per block
+  const int rofs = KG > 1 ? (32 / KG) * kg : 0;
   if constexpr (KG > 1) {
-    // groups 1 .. KG-1 leave their sums in LDS; group 0 adds them in group order
-    float* mg = reinterpret_cast<float*>(smem) + (size_t)wave * (MI * NI * 16 + MI) * 64 + lane;
-    if (kg > 0) {
-      float* mk = mg + (size_t)(kg - 1) * MERGE1;
+    float* const mbase = reinterpret_cast<float*>(smem) + (size_t)(wave * 64 + lane) * MROW;
+    {
+      float* mw = mbase + (size_t)kg * MERGE1;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mk[((mi * NI + ni) * 16 + i) * 64] = acc[mi][ni][i];
+          for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<f32x4_v*>(mw + (mi * NI + ni) * 16 + i4 * 4) =
+                f32x4_v{acc[mi][ni][i4 * 4], acc[mi][ni][i4 * 4 + 1], acc[mi][ni][i4 * 4 + 2],
+                        acc[mi][ni][i4 * 4 + 3]};
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) mk[(MI * NI * 16 + mi) * 64] = ssq[mi];
+      for (int mi = 0; mi < MI; ++mi) mw[MI * NI * 16 + mi] = ssq[mi];
     }
-    lds_barrier();  // the other groups' sums are in LDS
-    if (kg == 0) {
+    lds_barrier();  // every group's sums are in LDS
 #pragma unroll
-      for (int g = 0; g < KG - 1; ++g) {
-        const float* mk = mg + (size_t)g * MERGE1;
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
+        for (int e4 = 0; e4 < IE / 4; ++e4) {
+          f32x4_v t = *reinterpret_cast<const f32x4_v*>(mbase + (mi * NI + ni) * 16 + kg * IE + e4 * 4);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mi][ni][i] += mk[((mi * NI + ni) * 16 + i) * 64];
+          for (int g = 1; g < KG; ++g)
+            t += *reinterpret_cast<const f32x4_v*>(mbase + (size_t)g * MERGE1 + (mi * NI + ni) * 16 +
+                                                   kg * IE + e4 * 4);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) ssq[mi] += mk[(MI * NI * 16 + mi) * 64];
-      }
+          for (int e = 0; e < 4; ++e) acc[mi][ni][e4 * 4 + e] = t[e];
+        }
+      float q = mbase[MI * NI * 16 + mi];
+#pragma unroll
+      for (int g = 1; g < KG; ++g) q += mbase[(size_t)g * MERGE1 + MI * NI * 16 + mi];
+      ssq[mi] = q;
     }
     lds_barrier();  // merge reads done before the epilogue stages through the same LDS
-    if (kg > 0) return;
   }
 
   // ------------------------------------------------------------------ epilogue
@@ -330,8 +347,8 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
                                                        __float_as_uint(ssq[mi]), false, false);
       const float full = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float ss = __shfl(full, mfma32_row(i, lane), kWave);
+      for (int i = 0; i < IE; ++i) {
+        const float ss = __shfl(full, mfma32_row(i, lane) + rofs, kWave);
         const float rs = rsqrtf(ss / (float)K + qe.eps);
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni][i] *= rs;
@@ -343,8 +360,8 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
+      for (int i = 0; i < IE; ++i) {
+        const int row = min(row_base + mi * 32 + rofs + mfma32_row(i, lane), M - 1);
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni][i] += to_f32<T>(res[(size_t)row * se.ldc + n0 + wn * 32 * NI + ni * 32 + c32]);
@@ -401,22 +418,22 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
         if constexpr (kShareAngles) {  // kind != 2 implies share here
           const float4* ang4 = reinterpret_cast<const float4*>(smem) + (wm * MI + mi) * 16 * 64 + lane;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
+          for (int i = 0; i < IE; ++i) {
             const float4 a = ang4[i * 64];
             cs0[i] = make_float2(a.x, a.y);
             cs1[i] = make_float2(a.z, a.w);
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = min(row_base + mi * 32 + mfma32_row(i, lane), M - 1);
+          for (int i = 0; i < IE; ++i) {
+            const int row = min(row_base + mi * 32 + rofs + mfma32_row(i, lane), M - 1);
             const int pos = qe.positions[row];
             rope_sincos(pos, w0h, w0l, &cs0[i].y, &cs0[i].x);
             rope_sincos(pos, w1h, w1l, &cs1[i].y, &cs1[i].x);
           }
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < IE; ++i) {
           float v0 = acc[mi][0][i], v1 = acc[mi][1][i], v2 = acc[mi][2][i], v3 = acc[mi][3][i];
           // RMS over the head's 128 columns: 4 per lane, 32 lanes per half-wave.
           const float ss = half_wave_sum(v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3);
@@ -458,12 +475,13 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
     constexpr int LDW = WCOLS + 8;
     constexpr int CPR = WCOLS / 8;        // 16-byte chunks per row
     static_assert(NT / 64 * (32 * MI) * LDW <= SMEM, "staging does not fit");
-    T* st = smem + wave * (32 * MI) * LDW;
+    constexpr int RB = 32 / (KG > 1 ? KG : 1);  // rows of each 32-row block this wave finishes
+    T* st = smem + (kg * (NT / 64) + wave) * (RB * MI) * LDW;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = mi * 32 + mfma32_row(i, lane);
+      for (int i = 0; i < IE; ++i) {
+        const int r = mi * RB + mfma32_row(i, lane);
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) st[r * LDW + ni * 32 + c32] = from_f32<T>(acc[mi][ni][i]);
       }
@@ -471,17 +489,18 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
     __builtin_amdgcn_wave_barrier();
     constexpr int RPI = 64 / CPR;         // rows per wave instruction
 #pragma unroll 4
-    for (int r0 = 0; r0 < 32 * MI; r0 += RPI) {
+    for (int r0 = 0; r0 < RB * MI; r0 += RPI) {
       const int r = r0 + lane / CPR, ch = lane % CPR;
-      const int row = row_base + r;
-      if (row < M) st16(dst_row(row) + ch * 8, ld16(st + r * LDW + ch * 8));
+      const int row = row_base + (r / RB) * 32 + rofs + r % RB;
+      if ((RPI <= RB * MI || r < RB * MI) && row < M)
+        st16(dst_row(row) + ch * 8, ld16(st + r * LDW + ch * 8));
     }
   } else {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = row_base + mi * 32 + mfma32_row(i, lane);
+      for (int i = 0; i < IE; ++i) {
+        const int row = row_base + mi * 32 + rofs + mfma32_row(i, lane);
         if (row < M) {
           T* dst = dst_row(row) + c32;
 #pragma unroll
