@@ -267,11 +267,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
   // Merge the four 16-lane groups of the wave (lanes oct, oct+16, +32, +48).
 #pragma unroll
   for (int r = 0; r < NREP; ++r) {
-    const float M = wave_xor_max(m[r], 16, 32);
+    const float M = xor32_max(xor16_max(m[r]));
     const float sc = (m[r] == -INFINITY) ? 0.f : exp2f(m[r] - M);
-    l[r] = wave_xor_sum(l[r] * sc, 16, 32);
+    l[r] = xor32_sum(xor16_sum(l[r] * sc));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = wave_xor_sum(acc[r][e] * sc, 16, 32);
+    for (int e = 0; e < 8; ++e) acc[r][e] = xor32_sum(xor16_sum(acc[r][e] * sc));
     m[r] = M;
   }
 

@@ -154,18 +154,40 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Sum over the 32 lanes of each half-wave (lanes 0-31 and 32-63) with DPP
-// row permutes and one ds_swizzle; every lane of a half gets the half's sum.
+// row permutes and one 16-lane row swap; every lane of a half gets the
+// half's sum.
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
+// v + the value of lane l ^ 16 (v_permlane16_swap: the odd 16-lane rows of one
+// copy trade places with the even rows of the other, so the two results hold,
+// in every lane, its own row's value and its partner row's) -- a VALU op, no
+// LDS round trip.
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+// v + the value of lane l ^ 32 (v_permlane32_swap, the same with the two halves).
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
 __device__ __forceinline__ float half_wave_sum(float v) {
   v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]: xor 1
   v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]: xor 2
   v += dpp_move<0x141>(v);  // row_half_mirror: the other quad of each 8
   v += dpp_move<0x140>(v);  // row_mirror: the other 8 of each 16
-  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
-  return v;
+  return xor16_sum(v);      // the other 16 of each 32
 }
 
 // Sum over each 16-lane DPP row (lanes 16r .. 16r+15); every lane of the row
@@ -178,14 +200,5 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// xor-butterfly reductions across lanes.
-__device__ __forceinline__ float wave_xor_sum(float v, int mask_lo, int mask_hi) {
-  for (int m = mask_lo; m <= mask_hi; m <<= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-__device__ __forceinline__ float wave_xor_max(float v, int mask_lo, int mask_hi) {
-  for (int m = mask_lo; m <= mask_hi; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
 
 }  // namespace q3
