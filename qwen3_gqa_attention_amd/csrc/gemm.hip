@@ -491,7 +491,7 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
 #pragma unroll 4
     for (int r0 = 0; r0 < RB * MI; r0 += RPI) {
       const int r = r0 + lane / CPR, ch = lane % CPR;
-      const int row = row_base + (r / RB) * 32 + rofs + r % RB;
+      const int row = KG > 1 ? row_base + (r / RB) * 32 + rofs + r % RB : row_base + r;
       if ((RPI <= RB * MI || r < RB * MI) && row < M)
         st16(dst_row(row) + ch * 8, ld16(st + r * LDW + ch * 8));
     }
