@@ -51,12 +51,21 @@ PREFILL_TRAFFIC_KEY = {"attention": "prefill_attention", "qkv_norm_rope_gemm": "
                        "o_proj_gemm": "prefill_oproj"}
 
 
+def code_only(text):
+    """C++ source without its comments, trailing blanks and blank lines (an
+    edit to comments alone does not change a kernel)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash(key):
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[key]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

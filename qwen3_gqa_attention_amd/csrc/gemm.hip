@@ -102,11 +102,11 @@ __device__ __forceinline__ int swz(int row, int k) {
 // carry none of this (the residual loads would raise register pressure).
 //
 // KG = 2 or 4 splits the K range of each tile over KG groups of WM x WN
-// waves, each with its own LDS stages; groups 1 .. KG-1 hand their
-// accumulators to group 0 through LDS after the main loop, and group 0 runs
-// the epilogue.  Used when there is one tile per CU: more waves per SIMD, so
-// one wave's MFMAs cover the others' LDS and barrier waits, and more loads
-// in flight per CU.
+// waves, each with its own LDS stages.  After the main loop every group
+// leaves its accumulators in LDS, and each group sums (in group order) and
+// finishes 1/KG of the tile's rows.  Used when there is one tile per CU:
+// more waves per SIMD, so one wave's MFMAs cover the others' LDS and barrier
+// waits, and more loads in flight per CU.
 template <typename T, int WM, int WN, int MI, int NI, bool QKV, bool PARTIAL = false,
           int NSTAGE = 2, bool NORM = false, int KG = 1>
 __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __restrict__ A,
@@ -799,7 +799,7 @@ __global__ __launch_bounds__(64) void sum_partials_kernel(const float* __restric
 
 constexpr int kCus = 256;
 
-// Two K groups need an even number of 128-byte k-tiles.
+// K groups need a number of 128-byte k-tiles divisible by the group count.
 template <typename T>
 static bool k_groups_fit(int K, int groups = 2) {
   return (K / (128 / (int)sizeof(T))) % groups == 0;

@@ -98,3 +98,18 @@ def test_duration_timed_entries_run_long_enough():
     assert bench.steps_for_duration(2e-3) == max(bench.MIN_TIMED_STEPS, 100)
     assert bench.steps_for_duration(6.4e-5) * 6.4e-5 >= bench.MIN_TIMED_S
     assert bench.steps_for_duration(10.0) == bench.MIN_TIMED_STEPS
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    # the traffic figures stay valid across comment edits, not across code edits
+    names = bench.KERNEL_SOURCES["prefill_attention"]
+    for n in names:
+        (tmp_path / n).write_text(open(os.path.join(bench.CSRC, n)).read())
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    base = bench.kernel_source_hash("prefill_attention")
+    f = tmp_path / names[0]
+    src = f.read_text()
+    f.write_text("// a new comment line\n" + src.replace("\n", "  // note\n", 3) + "\n/* block\n comment */\n")
+    assert bench.kernel_source_hash("prefill_attention") == base
+    f.write_text(src.replace("kHeadDim", "kHeadDim + 0", 1))
+    assert bench.kernel_source_hash("prefill_attention") != base
