@@ -67,10 +67,12 @@ def element_bars(ref, dtype) -> np.ndarray:
 
 # Where exact arithmetic that keeps the block's bf16 storage points already
 # misses the bar (the storage floor below), the GPU may exceed the bar by at
-# most this factor over the floor's own worst element.  It covers the two
-# roundings the floor does not model: the attention probabilities held in
-# bf16 for the PV product, and fp32 summation order.
-FLOOR_ALLOWANCE = 1.15
+# most this factor over the floor's own worst element.  It covers what the
+# floor does not model: the softmax reference the kernels round the bf16
+# probabilities against (a fixed score bound or a running max rather than the
+# row's max, which changes which way each probability rounds) and fp32
+# summation order.  The largest ratio measured is 1.056 (64/4 heads, T=260).
+FLOOR_ALLOWANCE = 1.08
 
 
 def bf16(a) -> np.ndarray:
@@ -78,13 +80,35 @@ def bf16(a) -> np.ndarray:
     return bf16_bits_to_f32(round_to_bf16_bits(np.asarray(a, np.float32))).astype(np.float64)
 
 
+def attention_bf16_probs(q, k, v, window=None):
+    """Causal GQA for one sequence (the oracle's gqa_attention: same shapes, same
+    mask) with the attention probabilities held in bf16, as the PV product takes
+    them: p_j = bf16(exp(s_j - max_j s_j)), out = sum_j p_j v_j / sum_j p_j."""
+    T, n_q, dh = q.shape
+    S, n_kv, _ = k.shape
+    n_rep = n_q // n_kv
+    last = (S - T + np.arange(T))[:, None]
+    visible = np.arange(S)[None, :] <= last
+    if window:
+        visible &= np.arange(S)[None, :] > last - window
+    out = np.empty_like(q)
+    for h in range(n_q):
+        g = h // n_rep
+        s = np.where(visible, (q[:, h, :] @ k[:, g, :].T) / np.sqrt(dh), -np.inf)
+        p = bf16(np.exp(s - s.max(axis=1, keepdims=True)))
+        out[:, h, :] = (p @ v[:, g, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
 def storage_floor_rows(x, wq, wk, wv, wo, gq, gk, positions, ts, *, n_q, n_kv, window=None,
                        g_in=None, past_k=None, past_v=None) -> np.ndarray:
     """The block output at token rows ts of ONE sequence, computed exactly except for
     the roundings to bf16 that the block's storage fixes: the folded input-norm
-    weights W * g_in (layer variant), q~, k~ and v (the caches are bf16), the merged
-    attention output A (the bf16 o_proj input) and Y itself.  Everything else -- the
-    projections, QK-Norm, RoPE, softmax, the sums -- is the oracle's exact math.
+    weights W * g_in (layer variant), q~, k~ and v (the caches are bf16), the
+    attention probabilities (the bf16 operand of the PV product, relative to the
+    row's max score), the merged attention output A (the bf16 o_proj input) and Y
+    itself.  Everything else -- the projections, QK-Norm, RoPE, the softmax
+    statistics, the sums -- is the oracle's exact math.
     It is the error floor of any bf16 implementation with these storage points.
 
     x [T, d], positions [T]; past_k / past_v [n_kv, P, dh] (already bf16 values) for a
@@ -113,7 +137,7 @@ def storage_floor_rows(x, wq, wk, wv, wo, gq, gk, positions, ts, *, n_q, n_kv, w
     P = k.shape[0] - tmax
     out = []
     for i, t in enumerate(ts):
-        a = oracle.gqa_attention(q[i:i + 1], k[:P + t + 1], v[:P + t + 1], window)
+        a = attention_bf16_probs(q[i:i + 1], k[:P + t + 1], v[:P + t + 1], window)
         y = bf16(oracle.merge_heads(a)) @ f(wo).T
         if g_in is not None:
             y = y + xb[t]

@@ -2,7 +2,8 @@
 
 The bf16 bar is |got_i - ref_i| <= 2e-2 * max(1, |ref_i| / 4).  Where exact
 arithmetic that keeps the block's bf16 storage points (q~, k~, v in the bf16
-caches, the bf16 o_proj input A, Y) already misses it, a bf16 implementation
+caches, the bf16 attention probabilities, the bf16 o_proj input A, Y) already
+misses it, a bf16 implementation
 cannot meet it; these tests show on which workload that happens, with the
 oracle alone (no GPU)."""
 import numpy as np
