@@ -191,11 +191,13 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
   // still in flight (loads complete in issue order; s_waitcnt vmcnt(n) with
   // the other counters left alone).
   constexpr int INS = A_INS + B_INS;
-  static_assert(2 * INS < 64, "vmcnt range");
+  static_assert((NSTAGE - 1) * INS < 64, "vmcnt range");
   auto wait_tiles = [](int ahead) {
-    if (NSTAGE >= 4 && ahead >= 2) {
+    if (NSTAGE >= 4 && ahead >= 3) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((3 * INS) & 15) | (((3 * INS) >> 4) << 14));
+    } else if (NSTAGE >= 3 && ahead >= 2) {
       __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * INS) & 15) | (((2 * INS) >> 4) << 14));
-    } else if (NSTAGE >= 3 && ahead >= 1) {
+    } else if (ahead >= 1) {
       __builtin_amdgcn_s_waitcnt(0x0F70 | (INS & 15) | ((INS >> 4) << 14));
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -221,18 +223,25 @@ __global__ __launch_bounds__(WM * WN * 64 * KG) void gemm_nt_kernel(const T* __r
   }
   const int arow = wm * 32 * MI + c32;   // this lane's first A row in the tile
   const int brow = wn * 32 * NI + c32;   // this lane's first B row in the tile
-  // NSTAGE LDS buffers; k-tile kt lives in buffer kt % NSTAGE and its loads
-  // are issued NSTAGE - 1 tiles ahead.
+  // NSTAGE LDS buffers; k-tile kt lives in buffer kt % NSTAGE.  Every buffer
+  // is free at the start, so the first NSTAGE tiles are issued at once (the
+  // second tile's latency hides behind the first's); after that, tile
+  // kt + NSTAGE - 1 is issued at iteration kt >= 1, into the buffer tile
+  // kt - 1 has just released.
+  // (0.6B q/k/v 45.2 -> 44.7 us, 4B o_proj 98.7 -> 96.9 us against issuing
+  // NSTAGE - 1 tiles first; two alternating runs on one box)
 #pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st)
+  for (int st = 0; st < NSTAGE; ++st)
     if (st < KT) gload_lds(st, st * BK);
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt % NSTAGE;
-    wait_tiles(min(NSTAGE - 2, KT - 1 - kt));  // tile kt has landed (this wave's part)
+    // tile kt has landed (this wave's part): the tiles issued after it may
+    // still be in flight
+    wait_tiles(min(kt == 0 ? NSTAGE - 1 : NSTAGE - 2, KT - 1 - kt));
     lds_barrier();                             // ... and every wave's; tile kt-1 is consumed
     // The buffer refilled here held tile kt-1, which every wave finished
     // reading before the barrier above.
-    if (kt + NSTAGE - 1 < KT) gload_lds((kt + NSTAGE - 1) % NSTAGE, (kt + NSTAGE - 1) * BK);
+    if (kt > 0 && kt + NSTAGE - 1 < KT) gload_lds((kt + NSTAGE - 1) % NSTAGE, (kt + NSTAGE - 1) * BK);
     const T* as = gsm + buf * STAGE;
     const T* bs = as + BM * BK;
     // Fragments are double-buffered in registers: the LDS reads of k-step
