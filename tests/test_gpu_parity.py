@@ -182,10 +182,11 @@ def test_prefill_mha_case():
     assert_close(got["Y"], ref["Y"], w.dtype, "Y (MHA)")
 
 
-@pytest.mark.parametrize("n_q,n_kv,T", [(24, 8, 300), (40, 8, 190), (12, 4, 77)])
+@pytest.mark.parametrize("n_q,n_kv,T", [(24, 8, 300), (40, 8, 190), (12, 4, 77), (48, 8, 100),
+                                        (56, 8, 150)])
 def test_prefill_odd_group_sizes(n_q, n_kv, T):
-    # n_rep = 3 and 5: a wave's 32 packed rows cover a token range that is
-    # not aligned to the 64-key tiles.
+    # n_rep = 3, 5, 6 and 7: a wave's 32 packed rows cover a token range that
+    # is not aligned to the 64-key tiles.
     w = dataclasses.replace(WORKLOADS[2], n_q=n_q, n_kv=n_kv)
     say(f"prefill parity: n_q={n_q} n_kv={n_kv} T={T}")
     inp = prefill_inputs(w, B=1, T=T)
@@ -409,7 +410,8 @@ def check_decode(w, inp, kc_host, vc_host, got):
 
 
 @pytest.mark.parametrize("dtype,n_q,n_kv", [("bf16", 16, 8), ("f32", 16, 8), ("bf16", 32, 8),
-                                            ("bf16", 64, 4), ("bf16", 40, 8), ("bf16", 8, 8)])
+                                            ("bf16", 64, 4), ("bf16", 40, 8), ("bf16", 8, 8),
+                                            ("bf16", 24, 8), ("bf16", 48, 8)])
 def test_decode_parity_ragged(dtype, n_q, n_kv):
     w = dataclasses.replace(WORKLOADS[5], dtype=dtype, n_q=n_q, n_kv=n_kv)
     say(f"decode parity: dtype={dtype} n_q={n_q} n_kv={n_kv}")
