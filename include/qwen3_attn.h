@@ -21,7 +21,9 @@
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
  *     of the descriptor's dtype (fp32 or bf16) unless stated otherwise;
- *     positions are int32.  Accumulation is always fp32.
+ *     positions are int32 in [0, 2^24) (16,777,216: every such position is
+ *     exact in fp32, and the RoPE angle is formed from it exactly).
+ *     Accumulation is always fp32.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call is
  *     asynchronous on that stream and never synchronises the host.
  *   - Arguments are validated on the host before anything is enqueued: on any

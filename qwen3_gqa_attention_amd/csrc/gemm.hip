@@ -58,7 +58,8 @@ constexpr int kXcds = 8;
 // revolutions exactly -- p * hi is split into its rounded value and its
 // rounding error with one fma, and fract() of a float is exact -- so the
 // hardware sin/cos (which take revolutions) see an argument in [0, 1)
-// accurate to about 2^-24 revolutions at any position.
+// accurate to about 2^-24 revolutions for every position below 2^24 (the
+// supported range: such positions convert to float exactly).
 __device__ __forceinline__ void rope_sincos(int pos, float whi, float wlo, float* s, float* c) {
   const float p = static_cast<float>(pos);
   const float r = p * whi;

@@ -208,6 +208,20 @@ def test_prefill_nonzero_positions():
     assert_close(got["Y"], ref["Y"], w.dtype, "Y")
 
 
+def test_prefill_positions_at_the_top_of_the_supported_range():
+    # Positions up to 2^24 - 1 convert to fp32 exactly and the angle is reduced
+    # exactly in revolutions, so fp32 q~ and K keep the 1e-4 bar there.
+    w = WORKLOADS[1]
+    inp = prefill_inputs(w, B=1, T=40)
+    inp["positions"] = inp["positions"] + np.int32((1 << 24) - 40)
+    say(f"prefill parity at positions {int(inp['positions'].min())}..{int(inp['positions'].max())}")
+    got = run_prefill_gpu(w, inp, 1, 40)
+    ref = oracle_prefill(inp, w)
+    assert_close(got["Q"], ref["Q"], w.dtype, "q~")
+    assert_close(got["Kc"][:, :, :40], ref["Kc"], w.dtype, "k cache")
+    assert_close(got["Y"], ref["Y"], w.dtype, "Y")
+
+
 def test_prefill_deterministic_and_causal():
     w = WORKLOADS[2]
     inp = prefill_inputs(w, B=1, T=200)
